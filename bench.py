@@ -1,0 +1,386 @@
+#!/usr/bin/env python3
+"""Benchmark of the indexer hot path on one MI355X.
+
+A step is one call of the hot path over one batch of synthetic input that is
+already resident in HBM. By default the workload is the variable-length decode
+batch (B=4 requests, 4 bf16 query heads, 128 dims, 8192-block padded tables,
+seq_len 4096..131072 tokens at 16 tokens per block, K=256) through the fused
+idx_select. The timed steps rotate over enough copies of the inputs (over
+512 MiB) that every step reads its centroids from HBM, not from L2 or the
+256 MiB last-level cache.
+
+Prints one JSON line:
+  value         valid blocks scored + selected per second (whole job, 1 GPU)
+  ms_per_step   HIP-event time per step over the timed region
+  roofline      the dominant kernel: algorithmic bytes (or flops) per launch /
+                average launch time, against the MI355X peak
+  cpu_baseline  the CPU oracle on the host cores, on a bounded sample
+
+Other modes:
+  --workload N         1..5 (1: tiny fp32, 2: default, 3: top-K stress,
+                       4: large GQA batch, 5: k-means assignment)
+  --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
+  --parse-pmc DIR      turn rocprofv3 --pmc output into a traffic summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "blocks scored+selected/sec and µs per indexer call; % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+ROTATE_BYTES = 512 << 20
+CALIB_BYTES = 1 << 30
+
+KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
+          4: "select_fused_kernel", 5: "assign_kernel"}
+SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
+           ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "api.cpp")]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for s in SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------------------
+# workloads: device inputs, one step, algorithmic bytes
+# ----------------------------------------------------------------------------------------
+class Indexer:
+    def __init__(self, x, torch, idx, copies):
+        from tests.helpers import to_dev
+        self.x, self.torch, self.idx = x, torch, idx
+        q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+        self.inputs = [(q, c, sl)] + [(q.clone(), c.clone(), sl.clone()) for _ in range(copies - 1)]
+        dev = q.device
+        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(x.B, dtype=torch.int32, device=dev)
+        nbytes = idx.idx_workspace_bytes(x.B, x.N_pad, x.H, x.K, 0)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        import oracle
+        self.nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+        elem = 2 if x.dtype == "bf16" else 4
+        self.units = int(self.nv.sum())
+        self.row_bytes = x.D * elem
+        # centroid rows that hold tokens + query heads + seq_len + ids written
+        self.alg_bytes = (self.units * self.row_bytes + x.q.size * elem + 4 * x.B + 4 * x.B * x.K)
+        self.alg_flops = 2 * self.units * x.D  # after summing the heads once per request
+
+    def step(self, i):
+        q, c, sl = self.inputs[i % len(self.inputs)]
+        self.idx.idx_select(q, c, sl, self.x.K, page_size=self.x.page_size, sorted=self.x.sorted,
+                            ids=self.ids, counts=self.counts, ws=self.ws)
+
+    def describe(self):
+        x = self.x
+        return {"workload": x.name, "call": "idx_select", "B": x.B, "H": x.H, "D": x.D,
+                "N_pad": x.N_pad, "page_size": x.page_size, "K": x.K, "sorted": x.sorted,
+                "inputs": x.dtype, "accumulate": "f32", "seq_len": [int(v) for v in x.seq_len]
+                if x.B <= 8 else f"{int(x.seq_len.min())}..{int(x.seq_len.max())}",
+                "valid_blocks": self.units, "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import oracle
+        x = self.x
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            S, _ = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+            oracle.select(S, self.nv, x.K, x.sorted)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        return self.units / med, f"the whole batch ({self.units} valid blocks), {len(times)} " \
+                                 f"calls, median {med * 1e3:.1f} ms per call"
+
+
+class Topk:
+    def __init__(self, x, torch, idx, copies):
+        from tests.helpers import to_dev
+        self.x, self.torch, self.idx = x, torch, idx
+        s = to_dev(x.scores)
+        self.inputs = [s] + [s.clone() for _ in range(copies - 1)]
+        B, N = x.scores.shape
+        self.ids = torch.empty(B, x.K, dtype=torch.int32, device=s.device)
+        self.counts = torch.empty(B, dtype=torch.int32, device=s.device)
+        self.units = B * N
+        self.alg_bytes = B * N * 4 + B * x.K * 4
+        self.alg_flops = 0
+
+    def step(self, i):
+        self.idx.idx_topk(self.inputs[i % len(self.inputs)], self.x.K, None, False, ids=self.ids,
+                          counts=self.counts)
+
+    def describe(self):
+        B, N = self.x.scores.shape
+        return {"workload": self.x.name, "call": "idx_topk", "rows": B, "N": N, "K": self.x.K,
+                "sorted": False, "inputs": "f32", "distributions": 9,
+                "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import oracle
+        x = self.x
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            oracle.select(x.scores, None, x.K, False)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        return self.units / med, f"all {x.scores.shape[0]} rows, {len(times)} calls, " \
+                                 f"median {med * 1e3:.1f} ms per call"
+
+
+class Assign:
+    def __init__(self, x, torch, idx, copies):
+        from tests.helpers import to_dev
+        self.x, self.torch, self.idx = x, torch, idx
+        xd, cd = to_dev(x.x), to_dev(x.c)
+        self.inputs = [(xd, cd)] + [(xd.clone(), cd.clone()) for _ in range(copies - 1)]
+        N, D = x.x.shape
+        C = x.c.shape[0]
+        self.assign = torch.empty(N, dtype=torch.int32, device=xd.device)
+        self.ws = torch.zeros(idx.idx_assign_workspace_bytes(C, D), dtype=torch.uint8,
+                              device=xd.device)
+        self.units = N
+        self.alg_bytes = N * D * 2 + C * D * 2 + N * 4
+        self.alg_flops = 2 * N * C * D
+
+    def step(self, i):
+        xd, cd = self.inputs[i % len(self.inputs)]
+        self.idx.idx_assign(xd, cd, assign=self.assign, ws=self.ws)
+
+    def describe(self):
+        N, D = self.x.x.shape
+        return {"workload": self.x.name, "call": "idx_assign", "N": N, "C": self.x.c.shape[0],
+                "D": D, "inputs": "bf16", "accumulate": "f32 (MFMA)",
+                "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import numpy as np
+        import oracle
+        x = self.x
+        n = 2048
+        times = []
+        t_end = time.perf_counter() + budget_s
+        i = 0
+        while time.perf_counter() < t_end or len(times) < 3:
+            rows = slice((i * n) % x.x.shape[0], (i * n) % x.x.shape[0] + n)
+            t0 = time.perf_counter()
+            oracle.assign(x.x[rows], x.c)
+            times.append(time.perf_counter() - t0)
+            i += 1
+        med = statistics.median(times)
+        return n / med, f"{n} of the {x.x.shape[0]} points per call, {len(times)} calls, " \
+                        f"median {med * 1e3:.1f} ms per call"
+
+
+def make(w, torch, idx, copies):
+    import synth
+    x = synth.workload(w)
+    if w in (1, 2, 4):
+        return Indexer(x, torch, idx, copies)
+    if w == 3:
+        return Topk(x, torch, idx, copies)
+    return Assign(x, torch, idx, copies)
+
+
+def input_bytes(w, x):
+    if w in (1, 2, 4):
+        return x.q.nbytes + x.c.nbytes
+    if w == 3:
+        return x.scores.nbytes
+    return x.x.nbytes + x.c.nbytes
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+# ----------------------------------------------------------------------------------------
+# rocprofv3 --pmc output -> traffic summary
+# ----------------------------------------------------------------------------------------
+def parse_pmc(dirs, out_path, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the benchmarked kernel, scaled
+    by what the same counter reads for the 1 GiB calibration copy."""
+    import csv
+    rows = []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {dirs}")
+    per = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        ctr = r.get("Counter_Name", "")
+        val = float(r.get("Counter_Value", 0))
+        disp = r.get("Dispatch_Id", "")
+        per.setdefault((ctr, name), {}).setdefault(disp, 0.0)
+        per[(ctr, name)][disp] += val
+    kern = KERNEL[workload]
+
+    def avg(ctr, match):
+        vals = [v for (c, n), d in per.items() if c == ctr and match(n) for v in d.values()]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and kern not in n
+    is_kern = lambda n: kern in n
+    res = {"kernel": kern, "workload": workload, "source_sha256": source_digest()}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        k, nk = avg(ctr, is_kern)
+        cal, nc = avg(ctr, is_copy)
+        if k is None:
+            continue
+        res[ctr + "_kib_per_dispatch"] = k
+        res[ctr + "_dispatches"] = nk
+        if cal:
+            scale = CALIB_BYTES / (cal * 1024.0)
+            res[ctr + "_calib_scale"] = scale
+            res[ctr.split("_")[0].lower() + "_bytes_per_launch"] = k * 1024.0 * scale
+    with open(out_path, "w") as f:
+        f.write(f"# HBM traffic of {kern} (workload {workload}) from rocprofv3 --pmc\n")
+        f.write("# byte counters scaled by (1 GiB) / (counter for a plain 1 GiB device copy)\n")
+        for k_, v in res.items():
+            f.write(f"{k_}={v}\n")
+    print(json.dumps(res))
+
+
+def read_traffic(workload):
+    p = os.path.join(ROOT, "profiles", f"traffic_w{workload}_{KERNEL[workload]}.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k] = v
+    if kv.get("source_sha256") != source_digest():
+        return None  # the kernel changed since the counters were taken
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except KeyError:
+        return None
+
+
+# ----------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibrate", action="store_true")
+    ap.add_argument("--parse-pmc", nargs="+", default=None)
+    ap.add_argument("--out", default=None)
+    a = ap.parse_args()
+
+    if a.parse_pmc:
+        out = a.out or os.path.join(ROOT, "profiles",
+                                    f"traffic_w{a.workload}_{KERNEL[a.workload]}.txt")
+        parse_pmc(a.parse_pmc, out, a.workload)
+        return 0
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the indexer's "
+              "requests, rows and points are independent, so a multi-GPU run is G copies of "
+              "this one on disjoint slices", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_scoring_top_amd as idx
+    idx.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    import synth
+    x0 = synth.workload(a.workload)
+    copies = max(1, min(256, -(-ROTATE_BYTES // input_bytes(a.workload, x0))))
+    del x0
+    log(f"[bench] workload {a.workload}: building inputs ({copies} copies)")
+    wl = make(a.workload, torch, idx, copies)
+
+    if a.pmc_calibrate:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for i in range(a.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(a.steps):
+        wl.step(a.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / a.steps
+    log(f"[bench] {ms * 1e3:.2f} us per step (events), {wall / a.steps * 1e6:.2f} us wall")
+
+    per_s = 1e3 / ms
+    if a.workload == 5:
+        bound, unit = "mfma", "TFLOP/s"
+        achieved = wl.alg_flops / (ms * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS
+    else:
+        bound, unit = "hbm", "GB/s"
+        achieved = wl.alg_bytes / (ms * 1e-3) / 1e9
+        peak = HBM_PEAK_GBS
+    traffic = read_traffic(a.workload)
+    out = {
+        "metric": METRIC,
+        "value": wl.units * per_s,
+        "unit": {5: "points/s"}.get(a.workload, "entries/s" if a.workload == 3 else "blocks/s"),
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "us_per_call": ms * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": wl.describe(),
+        "roofline": {"bound": bound, "kernel": KERNEL[a.workload], "achieved": achieved,
+                     "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": traffic,
+                     "alg_bytes_per_launch": wl.alg_bytes, "alg_flops_per_launch": wl.alg_flops},
+    }
+    if not a.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle (~{a.cpu_seconds:.0f} s)")
+        v, sample = wl.cpu_oracle(a.cpu_seconds)
+        out["cpu_baseline"] = {"value": v, "unit": out["unit"], "cores": blas_threads(),
+                               "kind": "oracle", "sample": sample}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,201 @@
+"""Python binding of libidx.so, the MI355X block-scoring + top-K indexer.
+
+Argument marshalling only: every function here checks tensor placement and
+layout, passes raw device pointers and the current HIP stream to the C ABI
+(include/idx.h) and returns the output tensors. All arithmetic runs in the HIP
+kernels; there is no fallback path. PyTorch supplies device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["idx_score", "idx_topk", "idx_select", "idx_assign", "idx_workspace_bytes",
+           "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
+           "lib_path", "load", "IDX_SORTED", "IdxError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libidx.so")
+
+IDX_F32, IDX_BF16 = 0, 1
+IDX_SORTED = 0x1
+IDX_CHUNK_SHIFT = 8
+
+_c_int, _c_size, _vp, _u32 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32
+_SIGS = {
+    "idx_score": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "idx_topk_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _u32]),
+    "idx_topk": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _u32, _vp, _c_size, _vp]),
+    "idx_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
+    "idx_select": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                            _c_int, _c_int, _u32, _vp, _c_size, _vp]),
+    "idx_assign_workspace_bytes": (_c_size, [_c_int, _c_int]),
+    "idx_assign": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int64, _c_int, _c_int, _c_int, _vp,
+                            _c_size, _vp]),
+    "idx_status_string": (ctypes.c_char_p, [_c_int]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class IdxError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {idx_status_string(status)} ({status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libidx.so (once). Raises if it has not been built: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(f"{_LIB_PATH} is missing; build it with "
+                                   "`python -m block_scoring_top_amd.build`")
+            lib = ctypes.CDLL(_LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.restype, fn.argtypes = res, args
+            _lib = lib
+    return _lib
+
+
+def idx_status_string(status: int) -> str:
+    return load().idx_status_string(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return IDX_F32
+    if t.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        return IDX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn, st):
+    if st != 0:
+        raise IdxError(fn, st)
+
+
+def _dev(*ts):
+    d = ts[0].device
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda or t.device != d:
+                raise ValueError("all tensors must live on the same GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+    return d
+
+
+# one zero-filled workspace per (entry point, device, stream); the indexer kernels
+# leave theirs zeroed
+_ws_cache: dict = {}
+
+
+def _workspace(device, nbytes, kind):
+    key = (kind, device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def idx_workspace_bytes(B, N_pad, H, K, flags=0) -> int:
+    return load().idx_workspace_bytes(B, N_pad, H, K, flags)
+
+
+def idx_topk_workspace_bytes(B, N, K, flags=0) -> int:
+    return load().idx_topk_workspace_bytes(B, N, K, flags)
+
+
+def idx_assign_workspace_bytes(C, D) -> int:
+    return load().idx_assign_workspace_bytes(C, D)
+
+
+def idx_score(q, c, seq_len, page_size=16, scores=None):
+    """scores[b,n] = sum_h q[b,h].c[b,n] for n < ceil(seq_len[b]/page_size), else -inf."""
+    lib = load()
+    dev = _dev(q, c, seq_len, scores)
+    B, H, D = q.shape
+    N_pad = c.shape[1]
+    if scores is None:
+        scores = torch.empty(B, N_pad, dtype=torch.float32, device=dev)
+    _check("idx_score", lib.idx_score(_ptr(q), _ptr(c), _ptr(seq_len), _ptr(scores), B, H, D,
+                                      N_pad, page_size, _dtype_code(q), _stream(dev)))
+    return scores
+
+
+def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None):
+    """Row-wise top-K indices (ties to the lower index), padded with -1."""
+    lib = load()
+    dev = _dev(scores, n_valid, ids, counts)
+    B, N = scores.shape
+    if ids is None:
+        ids = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    flags = IDX_SORTED if sorted else 0
+    nbytes = lib.idx_topk_workspace_bytes(B, N, K, flags)
+    ws = _workspace(dev, nbytes, "topk") if nbytes else None
+    _check("idx_topk", lib.idx_topk(_ptr(scores), _ptr(n_valid), _ptr(ids), _ptr(counts), B, N, K,
+                                    flags, _ptr(ws), nbytes, _stream(dev)))
+    return ids, counts
+
+
+def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False, ids=None,
+               counts=None, scores_out=None, ws=None, chunk_log2=0):
+    """Fused score + mask + top-K. Returns (ids, counts, scores_out or None)."""
+    lib = load()
+    dev = _dev(q, c, seq_len, ids, counts, scores_out, ws)
+    B, H, D = q.shape
+    N_pad = c.shape[1]
+    if ids is None:
+        ids = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    if return_scores and scores_out is None:
+        scores_out = torch.empty(B, N_pad, dtype=torch.float32, device=dev)
+    flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+    nbytes = lib.idx_workspace_bytes(B, N_pad, H, K, flags)
+    if ws is None:
+        ws = _workspace(dev, nbytes, "select")
+    _check("idx_select", lib.idx_select(_ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts),
+                                        _ptr(scores_out), B, H, D, N_pad, page_size, K,
+                                        _dtype_code(q), flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return ids, counts, scores_out
+
+
+def idx_assign(x, c, return_best=False, assign=None, best=None, ws=None):
+    """k-means assignment: argmax_j (2 x.c_j - |c_j|^2), ties to the lower j."""
+    lib = load()
+    dev = _dev(x, c, assign, best, ws)
+    N, D = x.shape
+    C = c.shape[0]
+    if assign is None:
+        assign = torch.empty(N, dtype=torch.int32, device=dev)
+    if return_best and best is None:
+        best = torch.empty(N, dtype=torch.float32, device=dev)
+    nbytes = lib.idx_assign_workspace_bytes(C, D)
+    if ws is None:
+        ws = _workspace(dev, nbytes, "assign")
+    _check("idx_assign", lib.idx_assign(_ptr(x), _ptr(c), _ptr(assign), _ptr(best), N, C, D,
+                                        _dtype_code(x), _ptr(ws), ws.numel(), _stream(dev)))
+    return assign, best

@@ -1,0 +1,60 @@
+"""Ahead-of-time build of libidx.so for gfx950 (hipcc for the kernels, g++ for the
+host-only C ABI layer). Run as `python -m block_scoring_top_amd.build`."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libidx.so")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include")]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
+
+HIP_SOURCES = ["indexer.hip", "assign.hip"]
+CXX_SOURCES = ["api.cpp"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    return r.stdout + r.stderr
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libidx.so (always rebuilds). Returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for s in HIP_SOURCES:
+        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, s),
+                     "-o", os.path.join(BUILD, s + ".o")])
+    for s in CXX_SOURCES:
+        jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s),
+                     "-o", os.path.join(BUILD, s + ".o")])
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        outs = list(ex.map(_run, jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,159 @@
+// C ABI of the indexer: host-side argument validation, workspace layout and
+// dispatch to the kernel launchers. Validation makes no HIP call, so every
+// error path runs (and is tested) on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "idx.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Blocks scored per workgroup: a power of two in [lo, 256] chosen so that the
+// grid holds about `target` workgroups over the padded tables; or the caller's
+// choice from the flags.
+int chunk_rows(int B, int N_pad, uint32_t flags, int lo, int target) {
+  const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
+  if (l != 0) return 1 << l;
+  const int64_t total = (int64_t)B * N_pad;
+  int c = lo;
+  while (c < 256 && total / (2 * c) >= target) c *= 2;
+  return c;
+}
+// idx_score: 256-thread workgroups, 16 rows per step, ~1024 of them (4 per CU)
+constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
+// idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~512 of
+// them); many requests -> 256-thread workgroups (16 rows per step, ~1024)
+constexpr int kWideMaxRequests = 32;
+constexpr int kWideChunkMin = 64, kWideTarget = 512;
+
+int check_chunk_flag(uint32_t flags) {
+  const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
+  if (l != 0 && (l < 4 || l > 14)) return IDX_ERR_INVALID_ARG;
+  if (flags & ~(IDX_SORTED | IDX_CHUNK_MASK)) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+int check_scoring_args(const void* q, const void* c, const int32_t* seq_len, int B, int H, int D,
+                       int N_pad, int page_size, idx_dtype dt) {
+  if (q == nullptr || c == nullptr || seq_len == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(c, 16) || !aligned(seq_len, 4)) return IDX_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || D < 1 || N_pad < 1 || page_size < 1) return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if ((int64_t)B * N_pad > kMaxRows) return IDX_ERR_INVALID_ARG;
+  if (H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
+  return IDX_OK;
+}
+
+int hip_status(int e) { return e == 0 ? IDX_OK : IDX_ERR_HIP; }
+
+// idx_select workspace: [arrival counters: a fixed 64 KiB, one u32 per request]
+// [staging: B rows of round_up(N_pad, 4) floats]. The counter area does not move
+// with the shape, so a workspace reused for a larger batch never finds staged
+// scores where its counters are.
+constexpr int kMaxRequests = 16384;
+constexpr size_t kTicketBytes = kMaxRequests * sizeof(uint32_t);
+int stage_stride(int N_pad) { return (int)round_up((size_t)N_pad, 4); }
+
+}  // namespace
+
+extern "C" {
+
+const char* idx_status_string(int status) {
+  switch (status) {
+    case IDX_OK: return "ok";
+    case IDX_ERR_INVALID_ARG: return "invalid argument";
+    case IDX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case IDX_ERR_WORKSPACE: return "workspace missing or too small";
+    case IDX_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int idx_score(const void* q, const void* c, const int32_t* seq_len, float* scores, int B, int H,
+              int D, int N_pad, int page_size, idx_dtype dt, void* stream) {
+  int st = check_scoring_args(q, c, seq_len, B, H, D, N_pad, page_size, dt);
+  if (st != IDX_OK) return st;
+  if (scores == nullptr || !aligned(scores, 4)) return IDX_ERR_INVALID_ARG;
+  return hip_status(idxk::launch_score(q, c, seq_len, scores, B, H, N_pad, page_size,
+                                       dt == IDX_BF16,
+                                       chunk_rows(B, N_pad, 0, kScoreChunkMin, kScoreTarget),
+                                       stream));
+}
+
+size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags) {
+  (void)B; (void)N; (void)K; (void)flags;
+  return 0;
+}
+
+int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts, int B,
+             int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (scores == nullptr || ids == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(scores, 16) || !aligned(ids, 4) || !aligned(n_valid, 4) || !aligned(counts, 4))
+    return IDX_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || K < 1) return IDX_ERR_INVALID_ARG;
+  if (flags & ~IDX_SORTED) return IDX_ERR_INVALID_ARG;
+  if ((int64_t)B * N > (int64_t(1) << 40) || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
+  const bool sorted = (flags & IDX_SORTED) != 0;
+  if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
+  const size_t need = idx_topk_workspace_bytes(B, N, K, flags);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return IDX_ERR_WORKSPACE;
+  return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted, stream));
+}
+
+size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {
+  (void)H; (void)K; (void)flags;
+  if (B < 1 || N_pad < 1) return 0;
+  return kTicketBytes + (size_t)B * stage_stride(N_pad) * sizeof(float);
+}
+
+int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids, int32_t* counts,
+               float* scores_out, int B, int H, int D, int N_pad, int page_size, int K,
+               idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_scoring_args(q, c, seq_len, B, H, D, N_pad, page_size, dt);
+  if (st != IDX_OK) return st;
+  if (ids == nullptr || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(scores_out, 4))
+    return IDX_ERR_INVALID_ARG;
+  if (K < 1 || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
+  if ((st = check_chunk_flag(flags)) != IDX_OK) return st;
+  if (B > kMaxRequests) return IDX_ERR_UNSUPPORTED;
+  const bool sorted = (flags & IDX_SORTED) != 0;
+  if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
+  const size_t need = idx_workspace_bytes(B, N_pad, H, K, flags);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
+  uint32_t* tickets = static_cast<uint32_t*>(ws);
+  float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
+  const bool wide = B <= kWideMaxRequests;
+  const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
+                         : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
+  return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad,
+                                        page_size, K, dt == IDX_BF16, sorted, chunk, wide,
+                                        tickets, stage, stage_stride(N_pad), stream));
+}
+
+size_t idx_assign_workspace_bytes(int C, int D) {
+  (void)D;
+  if (C < 1) return 0;
+  return round_up((size_t)C * sizeof(float), 256);
+}
+
+int idx_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C, int D,
+               idx_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  if (x == nullptr || c == nullptr || assign == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(c, 16) || !aligned(assign, 4) || !aligned(best, 4))
+    return IDX_ERR_INVALID_ARG;
+  if (N < 1 || N > kMaxRows || C < 1 || C > 65536 || D < 1) return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if (D != IDX_HEAD_DIM || dt != IDX_BF16) return IDX_ERR_UNSUPPORTED;
+  const size_t need = idx_assign_workspace_bytes(C, D);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 16)) return IDX_ERR_WORKSPACE;
+  return hip_status(idxk::launch_assign(x, c, assign, best, N, C, static_cast<float*>(ws), stream));
+}
+
+}  // extern "C"

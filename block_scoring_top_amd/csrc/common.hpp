@@ -1,0 +1,97 @@
+// Device helpers shared by the indexer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idxk {
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+
+// ---- bf16 -------------------------------------------------------------------------------
+// A bf16 value is the upper half of an fp32 value; widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---- order keys -------------------------------------------------------------------------
+// Unsigned keys whose integer order is the numeric order of the fp32 scores
+// ("Round 18 Track C", section 1 Target 1: the radix passes run over uint keys).
+// Negative values have all bits flipped, non-negative ones get the sign bit set;
+// -0.0 is first mapped to +0.0 so that equal scores have equal keys.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // order_key(-inf): never a candidate
+
+// ---- wave primitives --------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// number of set bits of m in lanes below the calling lane
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int l);
+template <>
+__device__ __forceinline__ uint32_t readlane<uint32_t>(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Data-parallel-primitive lane moves (DPP, GFX9 encodings): each reads another
+// lane's register inside the VALU, with no trip through LDS.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;    // row_shr:n = 0x110 + n, within 16-lane rows
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i of its row
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i of its half row
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // lanes whose source is outside the row, or whose row is masked off, read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (row scans, then the row
+// totals carried across rows by broadcasts)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_u32<kDppRowShr1>(v);
+  v += dpp_u32<kDppRowShr1 + 1>(v);
+  v += dpp_u32<kDppRowShr1 + 3>(v);  // row_shr:4 (lanes 0..3 see 0)
+  v += dpp_u32<kDppRowShr1 + 7>(v);  // row_shr:8
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+// sum over groups of 16 consecutive lanes; every lane of a group gets the same
+// value (the pairings are symmetric, so each lane adds the same operands)
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ int n_valid_blocks(int seq_len, int page_size, int n_pad) {
+  long long s = seq_len < 0 ? 0 : seq_len;
+  long long nv = (s + page_size - 1) / page_size;
+  return (int)(nv < n_pad ? nv : n_pad);
+}
+
+}  // namespace idxk

@@ -1,0 +1,155 @@
+// Kernels of the indexer path: score, top-K, fused score + top-K.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "score.hpp"
+#include "select.hpp"
+
+namespace idxk {
+
+constexpr int kScoreNT = 256;   // idx_score workgroup: 4 waves
+constexpr int kTopkNT = 1024;   // top-K workgroup: 16 waves
+constexpr int kTopkSlots = 8;   // register tile: 1024*8*4 = 32768 keys
+
+// ---- idx_score ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict__ q,
+                                                         const void* __restrict__ c,
+                                                         const int32_t* __restrict__ seq_len,
+                                                         float* __restrict__ scores, int H,
+                                                         int N_pad, int page_size, int chunk,
+                                                         int nchunk) {
+  const int b = blockIdx.x / nchunk;
+  const int ch = blockIdx.x - b * nchunk;
+  const int nv = n_valid_blocks(seq_len[b], page_size, N_pad);
+  const int r0 = ch * chunk;
+  const int r_end = min(r0 + chunk, N_pad);
+  const int r1 = min(r_end, nv);
+  float* dst = scores + (size_t)b * N_pad;
+  if (r1 > r0) {
+    float qs[8];
+    load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
+    score_rows<BF16, kScoreNT>(c, (size_t)b * N_pad, qs, r0, r1, dst);
+  }
+  fill_neg_inf(dst, max(r0, nv), r_end);
+}
+
+// ---- idx_topk ----------------------------------------------------------------------------
+template <bool SORTED>
+__global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__ scores,
+                                                       const int32_t* __restrict__ n_valid,
+                                                       int32_t* __restrict__ ids,
+                                                       int32_t* __restrict__ counts, int N,
+                                                       int K) {
+  __shared__ SelectSmem<kTopkNT, kTopkSlots, SORTED> sm;
+  const int b = blockIdx.x;
+  int n = N;
+  if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
+  select_row<kTopkNT, kTopkSlots, SORTED>(scores + (size_t)b * N, n, N, K, ids + (size_t)b * K,
+                                          counts ? counts + b : nullptr, sm);
+}
+
+// ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
+// NT threads per workgroup, select tile NT*SLOTS*4 keys.
+template <bool BF16, bool SORTED, int NT, int SLOTS>
+__global__ __launch_bounds__(NT) void select_fused_kernel(
+    const void* __restrict__ q, const void* __restrict__ c, const int32_t* __restrict__ seq_len,
+    int32_t* __restrict__ ids, int32_t* __restrict__ counts, float* __restrict__ scores_out,
+    int H, int N_pad, int page_size, int K, int chunk, int nchunk, uint32_t* tickets,
+    float* stage, int stage_stride) {
+  __shared__ SelectSmem<NT, SLOTS, SORTED> sm;
+  __shared__ int s_last;
+  const int b = blockIdx.x / nchunk;
+  const int ch = blockIdx.x - b * nchunk;
+  // the summed query and the request length are loaded together (one round trip)
+  float qs[8];
+  load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
+  const int nv = n_valid_blocks(seq_len[b], page_size, N_pad);
+  const int n_part = max(1, (nv + chunk - 1) / chunk);
+  const int r0 = ch * chunk;
+  const int r_end = min(r0 + chunk, N_pad);
+  if (ch >= n_part) {  // nothing to score here
+    if (scores_out != nullptr) fill_neg_inf(scores_out + (size_t)b * N_pad, r0, r_end);
+    return;
+  }
+  float* row = scores_out != nullptr ? scores_out + (size_t)b * N_pad
+                                     : stage + (size_t)b * stage_stride;
+  const int row_cap = scores_out != nullptr ? N_pad : stage_stride;
+  const int r1 = min(r_end, nv);
+  if (r1 > r0) score_rows<BF16, NT, true, (NT >= 1024 ? 2 : 4)>(c, (size_t)b * N_pad, qs, r0, r1, row);
+  if (scores_out != nullptr) fill_neg_inf(row, max(r0, nv), r_end);
+
+  // Hand-off without cache-wide fences: the scores above were written with
+  // agent-scope (write-through) stores; waiting for every outstanding memory
+  // operation of this wave, then a workgroup barrier, means all of them have
+  // completed before the ticket is taken. The last of the request's n_part
+  // chunks to take a ticket reads the row with agent-scope loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&tickets[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == (uint32_t)(n_part - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)  // ready for the next call on this workspace
+    __hip_atomic_store(&tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  select_row<NT, SLOTS, SORTED, true>(row, nv, row_cap, K, ids + (size_t)b * K,
+                                                  counts ? counts + b : nullptr, sm);
+}
+
+// ---- launchers ---------------------------------------------------------------------------
+int launch_score(const void* q, const void* c, const int32_t* seq_len, float* scores, int B,
+                 int H, int N_pad, int page_size, bool bf16, int chunk, void* stream) {
+  const int nchunk = (N_pad + chunk - 1) / chunk;
+  const dim3 grid((unsigned)B * nchunk), block(kScoreNT);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf16)
+    hipLaunchKernelGGL(score_kernel<true>, grid, block, 0, s, q, c, seq_len, scores, H, N_pad,
+                       page_size, chunk, nchunk);
+  else
+    hipLaunchKernelGGL(score_kernel<false>, grid, block, 0, s, q, c, seq_len, scores, H, N_pad,
+                       page_size, chunk, nchunk);
+  return (int)hipGetLastError();
+}
+
+int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                int B, int N, int K, bool sorted, void* stream) {
+  const dim3 grid((unsigned)B), block(kTopkNT);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sorted)
+    hipLaunchKernelGGL(topk_kernel<true>, grid, block, 0, s, scores, n_valid, ids, counts, N, K);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, grid, block, 0, s, scores, n_valid, ids, counts, N, K);
+  return (int)hipGetLastError();
+}
+
+int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                  int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
+                  int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
+                  float* stage, int stage_stride, void* stream) {
+  const int nchunk = (N_pad + chunk - 1) / chunk;
+  const dim3 grid((unsigned)B * nchunk);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // wide: 1024-thread workgroups (16 waves keep the selecting workgroup's SIMDs
+  // busy; for a few long requests); otherwise 256 threads (many requests)
+#define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_)                                                     \
+  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_>), grid, dim3(NT_), 0, s, q, c,     \
+                     seq_len, ids, counts, scores_out, H, N_pad, page_size, K, chunk, nchunk,  \
+                     tickets, stage, stage_stride)
+#define IDX_LAUNCH_FUSED_NT(BF, SO) \
+  if (wide) IDX_LAUNCH_FUSED(BF, SO, 1024, 2); else IDX_LAUNCH_FUSED(BF, SO, 256, 8)
+  if (bf16) {
+    if (sorted) { IDX_LAUNCH_FUSED_NT(true, true); }
+    else { IDX_LAUNCH_FUSED_NT(true, false); }
+  } else {
+    if (sorted) { IDX_LAUNCH_FUSED_NT(false, true); }
+    else { IDX_LAUNCH_FUSED_NT(false, false); }
+  }
+#undef IDX_LAUNCH_FUSED_NT
+#undef IDX_LAUNCH_FUSED
+  return (int)hipGetLastError();
+}
+
+}  // namespace idxk

@@ -1,0 +1,25 @@
+// Host-side launchers of the indexer kernels (defined in the .hip files).
+// Plain C++ declarations, no HIP types: the stream travels as void*.
+// Each returns 0 on success or the hipError_t of a failed launch.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace idxk {
+
+int launch_score(const void* q, const void* c, const int32_t* seq_len, float* scores, int B,
+                 int H, int N_pad, int page_size, bool bf16, int chunk, void* stream);
+
+int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                int B, int N, int K, bool sorted, void* stream);
+
+int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                  int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
+                  int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
+                  float* stage, int stage_stride, void* stream);
+
+int launch_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C,
+                  float* cnorm, void* stream);
+
+}  // namespace idxk

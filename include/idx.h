@@ -1,0 +1,165 @@
+/*
+ * idx.h -- C ABI of the block-scoring + top-K indexer for AMD MI355X (gfx950).
+ *
+ * The indexer of a block-sparse attention layer scores every block (page) of a
+ * request's KV cache by comparing the block's centroid with the request's query
+ * heads, masks blocks past the request's length, and keeps the K best blocks.
+ * Sources (web pages; cited by title and section):
+ *   [CS]  "Iterate Centroids Score" -- the centroid-scoring kernel of a
+ *         block-sparse-attention indexer: query rows against a table of block
+ *         centroids, scoring each request's candidate pages for the top-K stage;
+ *         the scorer writes into a caller-provided output buffer.
+ *   [TK]  "Iterate Topk" -- the top-K kernel: per-segment scores in, top-K
+ *         indices out; an 8-bit radix seed design.
+ *   [QS]  "Round 18 Track C: qsa_topk2 Register-Cached Keys & Barrier Reduction
+ *         + qsa_score Query Hoisting & Unrolling" -- section 1 (score kernel
+ *         with query heads hoisted into registers; 4-pass 8-bit radix select
+ *         over unsigned order keys with a 256-bin histogram), section 2 (ids
+ *         compared bitwise, ties and signed zeros included).
+ *   [KM]  "Export Cake KMeans plan-runtime suite" -- Summary: the k-means
+ *         assignment call on bf16 points and centroids, norms fused into it.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller; arrays are
+ *     dense, row-major, C-contiguous. The library never allocates, frees,
+ *     copies between host and device, or synchronises: each call validates its
+ *     arguments on the host, enqueues kernels on `stream` and returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
+ *     kernels run on the device that is current on the calling thread.
+ *   - On a validation failure a call returns a negative status and enqueues
+ *     nothing, so no output byte is written. IDX_ERR_HIP reports a failed
+ *     launch; faults inside a kernel surface at the caller's next synchronise.
+ *   - Pointers read with 16-byte vector loads must be 16-byte aligned (stated
+ *     per argument). Integer arrays must be 4-byte aligned.
+ *   - bf16 data is passed as raw 16-bit patterns (uint16_t storage).
+ *   - Workspace: a caller-owned device buffer of at least the size the
+ *     matching *_workspace_bytes() returns. An idx_select workspace must be
+ *     zero-filled once before its first use (its counter area is then returned
+ *     to zero by every call). One workspace may serve any sequence of calls on
+ *     one stream; calls that may overlap (other streams) need distinct
+ *     workspaces.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { IDX_F32 = 0, IDX_BF16 = 1 } idx_dtype;
+
+enum {
+  IDX_OK = 0,
+  IDX_ERR_INVALID_ARG = -1, /* null / misaligned pointer, size out of range   */
+  IDX_ERR_UNSUPPORTED = -2, /* legal but not built: head_dim != 128, K > 4096 sorted */
+  IDX_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+  IDX_ERR_HIP = -4          /* the HIP runtime refused the launch              */
+};
+
+/* flags */
+#define IDX_SORTED 0x1u /* ids ordered by (score descending, id ascending);
+                           default: ascending block id                        */
+/* Bits 8..12 of `flags` optionally fix log2 of the number of blocks scored by
+ * one workgroup (4..14); 0 lets the library choose. Results do not depend on it. */
+#define IDX_CHUNK_SHIFT 8
+#define IDX_CHUNK_MASK (0x1Fu << IDX_CHUNK_SHIFT)
+#define IDX_CHUNK_LOG2(l) ((uint32_t)(l) << IDX_CHUNK_SHIFT)
+
+/* Limits of this build. */
+#define IDX_HEAD_DIM 128     /* D: the only head dimension compiled            */
+#define IDX_MAX_HEADS 64     /* H                                              */
+#define IDX_MAX_SORTED_K 4096
+#define IDX_MAX_REQUESTS 16384 /* B of one idx_select call */
+
+/*
+ * Number of blocks of request b that hold tokens, used by every scoring call:
+ *     n_valid[b] = min(N_pad, ceil(seq_len[b] / page_size)).
+ * The partly filled last page is a candidate ([QS] section 1 counts a block for
+ * every started group of tokens: 8193 tokens in 4-token blocks are 2049 blocks).
+ */
+
+/*
+ * idx_score -- block scores ([CS]; [QS] section 1, Target 2).
+ *   scores[b,n] = sum_{h<H} sum_{d<D} q[b,h,d] * c[b,n,d]   for n <  n_valid[b]
+ *   scores[b,n] = -inf (bit pattern 0xFF800000)             for n >= n_valid[b]
+ * accumulated in fp32. Centroid rows at or past n_valid[b] are never read, so
+ * their contents are irrelevant (they may hold NaN).
+ *   q        [B,H,D]      dtype dt, 16-byte aligned
+ *   c        [B,N_pad,D]  dtype dt, 16-byte aligned
+ *   seq_len  [B] int32    tokens per request, 0 <= seq_len[b] <= N_pad*page_size
+ *                         (values are read on the device; an out-of-range value
+ *                         is clamped to that range, not reported)
+ *   scores   [B,N_pad] float32 output
+ * B >= 1, 1 <= H <= IDX_MAX_HEADS, D == IDX_HEAD_DIM, N_pad >= 1, page_size >= 1.
+ */
+int idx_score(const void* q, const void* c, const int32_t* seq_len, float* scores,
+              int B, int H, int D, int N_pad, int page_size, idx_dtype dt, void* stream);
+
+/*
+ * idx_topk -- row-wise top-K of given scores ([TK]; [QS] section 1 Target 1).
+ *   For each row b, candidates are the entries n < n_valid[b] (all N entries if
+ *   n_valid is NULL) whose score is not -inf. The selected set is the m =
+ *   min(K, #candidates) candidates with the largest scores; equal scores
+ *   (-0.0 == +0.0) go to the lower index. NaN scores are outside the contract.
+ *   ids[b, 0..m-1] receive the selected indices, in ascending index order by
+ *   default or by (score desc, index asc) with IDX_SORTED; ids[b, m..K-1] = -1.
+ *   counts[b] = m when counts is not NULL.
+ *   scores  [B,N] float32 (16-byte aligned)      n_valid [B] int32 or NULL
+ *   ids     [B,K] int32 output                    counts  [B] int32 output or NULL
+ * B >= 1, N >= 1, K >= 1 (K <= IDX_MAX_SORTED_K with IDX_SORTED).
+ * ws / ws_bytes: workspace of at least idx_topk_workspace_bytes() bytes (may be
+ * NULL when that is 0).
+ */
+size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags);
+int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+             int B, int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * idx_select -- fused score + mask + top-K ([CS] scorer feeding the top-K
+ * stage; [QS] section 1, "combined" = score then select). Same inputs as
+ * idx_score and the same selection rule as idx_topk applied to the scores that
+ * idx_score would produce; the ids do not depend on whether scores_out is given.
+ *   ids        [B,K] int32 output; counts [B] int32 output or NULL
+ *   scores_out [B,N_pad] float32 output or NULL: when given it receives exactly
+ *              what idx_score writes (for parity checks and debugging)
+ * K >= 1 (K <= IDX_MAX_SORTED_K with IDX_SORTED).
+ * B <= IDX_MAX_REQUESTS.
+ * ws / ws_bytes: workspace of at least idx_workspace_bytes(B, N_pad, H, K, flags)
+ * bytes, zero-filled before first use. Its first 64 KiB hold one arrival
+ * counter per request, which every call returns to zero; the rest stages the
+ * scores. The counter area has a fixed place, so one workspace may serve calls
+ * of any shape that fits it.
+ */
+size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags);
+int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+               int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
+               int page_size, int K, idx_dtype dt, uint32_t flags, void* ws,
+               size_t ws_bytes, void* stream);
+
+/*
+ * idx_assign -- nearest-centroid k-means assignment ([KM] Summary): the select
+ * step with K = 1 over a dense score matrix.
+ *   assign[i] = argmax_j ( 2 * x[i,:].c[j,:] - |c[j,:]|^2 ), ties to the lower j,
+ * products of bf16 values accumulated in fp32 on the matrix cores. The centroid
+ * norms are computed inside the call (the workspace holds them).
+ *   x      [N,D] bf16 (16-byte aligned)    c [C,D] bf16 (16-byte aligned)
+ *   assign [N] int32 output
+ *   best   [N] float32 output or NULL: the winning value of dot(x,c) - |c|^2/2
+ *          (half the score above), for parity checks
+ * N >= 1, 1 <= C <= 65536, D == IDX_HEAD_DIM, dt == IDX_BF16.
+ */
+size_t idx_assign_workspace_bytes(int C, int D);
+int idx_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N,
+               int C, int D, idx_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* idx_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

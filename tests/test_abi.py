@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status before any HIP
+call. Every call here fails validation, so no kernel is ever launched (the
+pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_scoring_top_amd as idx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+P = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(idx.lib_path()):
+        pytest.skip("libidx.so not built")
+    return idx.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for n in ["idx_score", "idx_topk", "idx_select", "idx_assign", "idx_workspace_bytes",
+              "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", idx.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert idx.idx_status_string(OK) == "ok"
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert idx.idx_status_string(s) not in ("ok", "unknown status")
+    assert idx.idx_status_string(12345) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    # a fixed 64 KiB of arrival counters, then B rows of round_up(N_pad, 4) floats
+    assert lib.idx_workspace_bytes(4, 8192, 4, 256, 0) == 65536 + 4 * 8192 * 4
+    assert lib.idx_workspace_bytes(1, 1001, 4, 8, 0) == 65536 + 1004 * 4
+    assert lib.idx_workspace_bytes(0, 10, 4, 8, 0) == 0
+    assert lib.idx_assign_workspace_bytes(1024, 128) == 4096
+    assert lib.idx_assign_workspace_bytes(1, 128) == 256
+
+
+def score_call(lib, **kw):
+    a = dict(q=P, c=P, seq_len=P, scores=P, B=1, H=4, D=128, N_pad=64, page_size=16, dt=1)
+    a.update(kw)
+    return lib.idx_score(a["q"], a["c"], a["seq_len"], a["scores"], a["B"], a["H"], a["D"],
+                         a["N_pad"], a["page_size"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(c=None), INVALID), (dict(seq_len=None), INVALID),
+    (dict(scores=None), INVALID), (dict(q=P + 8), INVALID), (dict(c=P + 4), INVALID),
+    (dict(seq_len=P + 2), INVALID), (dict(B=0), INVALID), (dict(H=0), INVALID),
+    (dict(N_pad=0), INVALID), (dict(page_size=0), INVALID), (dict(dt=7), INVALID),
+    (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(B=1 << 20, N_pad=1 << 12), INVALID),
+])
+def test_score_rejects(lib, kw, want):
+    assert score_call(lib, **kw) == want
+
+
+def topk_call(lib, **kw):
+    a = dict(scores=P, n_valid=None, ids=P, counts=None, B=2, N=100, K=10, flags=0, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return lib.idx_topk(a["scores"], a["n_valid"], a["ids"], a["counts"], a["B"], a["N"], a["K"],
+                        a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(scores=None), INVALID), (dict(ids=None), INVALID), (dict(scores=P + 4), INVALID),
+    (dict(ids=P + 2), INVALID), (dict(n_valid=P + 1), INVALID), (dict(counts=P + 3), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(K=0), INVALID), (dict(flags=0x80), INVALID),
+    (dict(K=4097, flags=1), UNSUPPORTED),
+])
+def test_topk_rejects(lib, kw, want):
+    assert topk_call(lib, **kw) == want
+
+
+def select_call(lib, **kw):
+    a = dict(q=P, c=P, seq_len=P, ids=P, counts=None, scores_out=None, B=2, H=4, D=128,
+             N_pad=100, page_size=16, K=10, dt=1, flags=0, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.idx_select(a["q"], a["c"], a["seq_len"], a["ids"], a["counts"], a["scores_out"],
+                          a["B"], a["H"], a["D"], a["N_pad"], a["page_size"], a["K"], a["dt"],
+                          a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(ids=None), INVALID), (dict(ids=P + 1), INVALID),
+    (dict(scores_out=P + 2), INVALID), (dict(K=0), INVALID), (dict(B=0), INVALID),
+    (dict(flags=0x4), INVALID), (dict(flags=3 << 8), INVALID),
+    (dict(flags=15 << 8), INVALID), (dict(D=256), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
+    (dict(B=16385, N_pad=4), UNSUPPORTED),
+])
+def test_select_rejects(lib, kw, want):
+    assert select_call(lib, **kw) == want
+
+
+def assign_call(lib, **kw):
+    a = dict(x=P, c=P, assign=P, best=None, N=1000, C=64, D=128, dt=1, ws=P, ws_bytes=4096)
+    a.update(kw)
+    return lib.idx_assign(a["x"], a["c"], a["assign"], a["best"], a["N"], a["C"], a["D"], a["dt"],
+                          a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), INVALID), (dict(c=None), INVALID), (dict(assign=None), INVALID),
+    (dict(x=P + 8), INVALID), (dict(best=P + 1), INVALID), (dict(N=0), INVALID),
+    (dict(C=0), INVALID), (dict(C=65537), INVALID), (dict(dt=0), UNSUPPORTED),
+    (dict(D=64), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=4), WORKSPACE),
+])
+def test_assign_rejects(lib, kw, want):
+    assert assign_call(lib, **kw) == want
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(idx, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(idx, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        idx.load()
