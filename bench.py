@@ -2,7 +2,9 @@
 """Benchmark of the indexer hot path on one MI355X.
 
 A step is one call of the hot path over one batch of synthetic input that is
-already resident in HBM. By default the workload is the variable-length decode
+already resident in HBM. The timed steps are captured once into a HIP graph and
+replayed, so the GPU runs them back to back; the host-launched (eager) time per
+call is reported beside it. By default the workload is the variable-length decode
 batch (B=4 requests, 4 bf16 query heads, 128 dims, 8192-block padded tables,
 seq_len 4096..131072 tokens at 16 tokens per block, K=256) through the fused
 idx_select. The timed steps rotate over enough copies of the inputs (over
@@ -60,12 +62,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def to_dev(a):
+    """numpy -> torch on cuda:0; bf16 bit patterns (uint16) become bfloat16 tensors."""
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(
+            torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
 # ----------------------------------------------------------------------------------------
 # workloads: device inputs, one step, algorithmic bytes
 # ----------------------------------------------------------------------------------------
 class Indexer:
     def __init__(self, x, torch, idx, copies):
-        from tests.helpers import to_dev
         self.x, self.torch, self.idx = x, torch, idx
         q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
         self.inputs = [(q, c, sl)] + [(q.clone(), c.clone(), sl.clone()) for _ in range(copies - 1)]
@@ -74,10 +85,10 @@ class Indexer:
         self.counts = torch.empty(x.B, dtype=torch.int32, device=dev)
         nbytes = idx.idx_workspace_bytes(x.B, x.N_pad, x.H, x.K, 0)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-        import oracle
-        self.nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+        # blocks holding tokens: ceil(seq_len / page_size), at most N_pad
+        self.nv = [min(x.N_pad, -(-int(v) // x.page_size)) for v in x.seq_len]
         elem = 2 if x.dtype == "bf16" else 4
-        self.units = int(self.nv.sum())
+        self.units = int(sum(self.nv))
         self.row_bytes = x.D * elem
         # centroid rows that hold tokens + query heads + seq_len + ids written
         self.alg_bytes = (self.units * self.row_bytes + x.q.size * elem + 4 * x.B + 4 * x.B * x.K)
@@ -113,7 +124,6 @@ class Indexer:
 
 class Topk:
     def __init__(self, x, torch, idx, copies):
-        from tests.helpers import to_dev
         self.x, self.torch, self.idx = x, torch, idx
         s = to_dev(x.scores)
         self.inputs = [s] + [s.clone() for _ in range(copies - 1)]
@@ -150,7 +160,6 @@ class Topk:
 
 class Assign:
     def __init__(self, x, torch, idx, copies):
-        from tests.helpers import to_dev
         self.x, self.torch, self.idx = x, torch, idx
         xd, cd = to_dev(x.x), to_dev(x.c)
         self.inputs = [(xd, cd)] + [(xd.clone(), cd.clone()) for _ in range(copies - 1)]
@@ -233,7 +242,7 @@ def parse_pmc(dirs, out_path, workload):
                 rows += list(csv.DictReader(fh))
     if not rows:
         raise SystemExit(f"no counter_collection.csv under {dirs}")
-    per = {}
+    per = {}  # (counter, kernel) -> {dispatch: value summed over counter instances}
     for r in rows:
         name = r.get("Kernel_Name", "")
         ctr = r.get("Counter_Name", "")
@@ -243,16 +252,23 @@ def parse_pmc(dirs, out_path, workload):
         per[(ctr, name)][disp] += val
     kern = KERNEL[workload]
 
+    def values(ctr, match):
+        return [v for (c, n), d in per.items() if c == ctr and match(n) for v in d.values()]
+
     def avg(ctr, match):
-        vals = [v for (c, n), d in per.items() if c == ctr and match(n) for v in d.values()]
+        vals = values(ctr, match)
         return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
-    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and kern not in n
+    def calib(ctr):
+        # the 1 GiB copy is the largest copy dispatch of the run
+        vals = values(ctr, lambda n: "copy" in n.lower() and kern not in n)
+        return (max(vals), 1) if vals else (None, 0)
+
     is_kern = lambda n: kern in n
     res = {"kernel": kern, "workload": workload, "source_sha256": source_digest()}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         k, nk = avg(ctr, is_kern)
-        cal, nc = avg(ctr, is_copy)
+        cal, nc = calib(ctr)
         if k is None:
             continue
         res[ctr + "_kib_per_dispatch"] = k
@@ -295,6 +311,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time host-launched steps instead of a replayed HIP graph")
     ap.add_argument("--pmc-calibrate", action="store_true")
     ap.add_argument("--parse-pmc", nargs="+", default=None)
     ap.add_argument("--out", default=None)
@@ -332,23 +350,54 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    # eager: one host call per step (Python binding -> C ABI -> launch)
     for i in range(a.warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
+    n_eager = min(a.steps, 500)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_eager):
+        wl.step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n_eager
+
+    # timed region: the K steps captured once into a HIP graph and replayed, so
+    # the GPU runs the steps back to back without waiting on the host
+    graph = None
+    if not a.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                wl.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(a.steps):
+                wl.step(a.warmup + i)
+        graph.replay()  # untimed warm replay
+        torch.cuda.synchronize()
+    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps "
+        f"({'graph replay' if graph else 'eager'})")
+    stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(a.steps):
-        wl.step(a.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(a.steps):
+            wl.step(a.warmup + i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / a.steps
-    log(f"[bench] {ms * 1e3:.2f} us per step (events), {wall / a.steps * 1e6:.2f} us wall")
+    log(f"[bench] {ms * 1e3:.2f} us per step (events), {wall / a.steps * 1e6:.2f} us wall, "
+        f"eager {eager_ms * 1e3:.2f} us per step")
 
     per_s = 1e3 / ms
     if a.workload == 5:
@@ -365,7 +414,8 @@ def main():
         "value": wl.units * per_s,
         "unit": {5: "points/s"}.get(a.workload, "entries/s" if a.workload == 3 else "blocks/s"),
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": ms, "us_per_call": ms * 1e3,
+        "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
+        "launch": "eager" if graph is None else f"hipGraph of {a.steps} steps",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": wl.describe(),

@@ -166,6 +166,36 @@ def test_select_workspace_reused_across_shapes():
         check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s.cpu().numpy(), nv, 64, False)
 
 
+def test_select_graph_replays_match_eager():
+    """idx_select captured into a HIP graph: every replay equals the eager call."""
+    x = synth.make_indexer(4, 4, 128, 8192, [4096, 16384, 65536, 131072], 256, "bf16", 310)
+    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+    ws = torch.zeros(idx.idx_workspace_bytes(4, 8192, 4, 256), dtype=torch.uint8, device="cuda")
+    ref, rc, _ = idx.idx_select(q, c, sl, 256, ws=ws)
+    ref, rc = ref.clone(), rc.clone()
+    ids = torch.full((4, 256), -7, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(4, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        idx.idx_select(q, c, sl, 256, ids=ids, counts=counts, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            idx.idx_select(q, c, sl, 256, ids=ids, counts=counts, ws=ws)
+    for rep in range(4):
+        say(f"[select] graph replay {rep}")
+        ids.fill_(-7)
+        counts.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref) and torch.equal(counts, rc), rep
+        eager, _, _ = idx.idx_select(q, c, sl, 256, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+
+
 def test_select_is_deterministic():
     x = synth.make_indexer(4, 4, 128, 8192, [4096, 16384, 65536, 131072], 256, "bf16", 305)
     a = run_select(x, 256, False, with_scores=True)
