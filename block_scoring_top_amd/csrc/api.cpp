@@ -28,10 +28,11 @@ int chunk_rows(int B, int N_pad, uint32_t flags, int lo, int target) {
 }
 // idx_score: 256-thread workgroups, 16 rows per step, ~1024 of them (4 per CU)
 constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
-// idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~512 of
-// them); many requests -> 256-thread workgroups (16 rows per step, ~1024)
+// idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~256 of
+// them: one per CU, all resident at once); many requests -> 256-thread
+// workgroups (16 rows per step, ~1024)
 constexpr int kWideMaxRequests = 32;
-constexpr int kWideChunkMin = 64, kWideTarget = 512;
+constexpr int kWideChunkMin = 64, kWideTarget = 256;
 
 int check_chunk_flag(uint32_t flags) {
   const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
@@ -53,12 +54,11 @@ int check_scoring_args(const void* q, const void* c, const int32_t* seq_len, int
 
 int hip_status(int e) { return e == 0 ? IDX_OK : IDX_ERR_HIP; }
 
-// idx_select workspace: [arrival counters: a fixed 64 KiB, one u32 per request]
-// [staging: B rows of round_up(N_pad, 4) floats]. The counter area does not move
-// with the shape, so a workspace reused for a larger batch never finds staged
-// scores where its counters are.
+// idx_select workspace: [arrival counters: a fixed 2 MiB, one 128-byte line per
+// request][staging: B rows of round_up(N_pad, 4) floats]. Every call returns all
+// of it to zero, so one workspace can serve calls of any shape that fits.
 constexpr int kMaxRequests = 16384;
-constexpr size_t kTicketBytes = kMaxRequests * sizeof(uint32_t);
+constexpr size_t kTicketBytes = kMaxRequests * size_t(128);
 int stage_stride(int N_pad) { return (int)round_up((size_t)N_pad, 4); }
 
 }  // namespace

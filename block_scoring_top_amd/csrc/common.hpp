@@ -26,6 +26,18 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // order_key(-inf): never a candidate
 
+// Radix digits of the keys, most significant first: 11 + 11 + 10 bits, so a row
+// is resolved in at most three histogram passes over 2048 bins.
+constexpr int kBins = 2048;
+constexpr int kDigit0Shift = 21;  // the first digit is key >> 21
+
+// ---- buffer loads ----------------------------------------------------------------------
+// Fourth dword of a raw buffer resource (32-bit data format) and the cache
+// policy bit that makes a load device-coherent (sc1: bypasses stale L2 lines of
+// other XCDs).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kCachePolicySc1 = 16;
+
 // ---- wave primitives --------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

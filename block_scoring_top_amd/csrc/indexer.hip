@@ -8,6 +8,9 @@
 namespace idxk {
 
 constexpr int kScoreNT = 256;   // idx_score workgroup: 4 waves
+// One arrival counter per request, each on its own 128-byte line: the atomics of
+// one line are serialised where they are performed, so requests must not share.
+constexpr int kTicketStride = 32;
 constexpr int kTopkNT = 1024;   // top-K workgroup: 16 waves
 constexpr int kTopkSlots = 8;   // register tile: 1024*8*4 = 32768 keys
 
@@ -83,20 +86,23 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   // agent-scope (write-through) stores; waiting for every outstanding memory
   // operation of this wave, then a workgroup barrier, means all of them have
   // completed before the ticket is taken. The last of the request's n_part
-  // chunks to take a ticket reads the row with agent-scope loads.
+  // chunks to take a ticket reads the row with agent-scope loads and returns
+  // the staged row to zero.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(&tickets[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(&tickets[(size_t)b * kTicketStride], 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == (uint32_t)(n_part - 1));
   }
   __syncthreads();
   if (!s_last) return;
   if (threadIdx.x == 0)  // ready for the next call on this workspace
-    __hip_atomic_store(&tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   select_row<NT, SLOTS, SORTED, true>(row, nv, row_cap, K, ids + (size_t)b * K,
-                                                  counts ? counts + b : nullptr, sm);
+                                      counts ? counts + b : nullptr, sm,
+                                      scores_out != nullptr ? nullptr : row);
 }
 
 // ---- launchers ---------------------------------------------------------------------------

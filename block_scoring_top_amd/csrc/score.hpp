@@ -98,10 +98,11 @@ __device__ __forceinline__ void score_rows(const void* c, size_t row_base, const
       acc = sum16(acc);
       const int r = base + u * ROWS_PER_STEP + my;
       if (l16 == 0 && r < r1) {
-        if constexpr (COHERENT)
+        if constexpr (COHERENT) {
           __hip_atomic_store(dst + r, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
+        } else {
           dst[r] = acc;
+        }
       }
     }
   }

@@ -30,12 +30,10 @@ namespace idxk {
 
 constexpr int kMaxSortedK = 4096;
 
-// Radix digits of the 32-bit keys, most significant first: 11 + 11 + 10 bits,
-// so a row is resolved in at most three histogram passes over 2048 bins.
 constexpr int kPasses = 3;
-constexpr int kCandCap = 512;  // threshold-bin keys resolved by counting instead of passes
-constexpr int kBins = 2048;
-__device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__device__ __forceinline__ int digit_shift(int p) {
+  return p == 0 ? kDigit0Shift : (p == 1 ? 10 : 0);
+}
 __device__ __forceinline__ uint32_t digit_mask(int p) { return p == 2 ? 0x3FFu : 0x7FFu; }
 
 template <int NT, int SLOTS, bool SORTED>
@@ -47,8 +45,6 @@ struct SelectSmem {
   uint32_t sel_bin, sel_need, sel_tot, n_cand;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
-  uint32_t n_in_bin, thr_key, thr_need;
-  alignas(16) uint32_t cand[kCandCap + 8];
   alignas(16) uint32_t skey[SORTED ? kMaxSortedK + 4 : 1];
   int32_t sid[SORTED ? kMaxSortedK : 1];
 };
@@ -66,8 +62,24 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int cap, int 
                                           uint32_t (&keys)[SLOTS][4]) {
   const int t = threadIdx.x;
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(row);
-  const bool vec = !COHERENT && (((uintptr_t)row & 15) == 0) && (cap & 3) == 0;
-  if (vec) {
+  const bool aligned4 = (((uintptr_t)row & 15) == 0) && (cap & 3) == 0;
+  if (COHERENT && aligned4) {
+    // 16-byte buffer loads with the device-scope cache policy (sc1); the buffer
+    // bounds are the row's readable bytes, past which a load returns zeros
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, cap * 4, kBufferDword3);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (base + i * NT * 4 < n) {
+        const int e0 = base + (i * NT + t) * 4;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, e0 * 4, 0, kCachePolicySc1);
+        keys[i][0] = v[0];
+        keys[i][1] = v[1];
+        keys[i][2] = v[2];
+        keys[i][3] = v[3];
+      }
+    }
+  } else if (!COHERENT && aligned4) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       if (base + i * NT * 4 < n) {  // uniform: some thread of the workgroup has data here
@@ -105,16 +117,24 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int cap, int 
   }
 }
 
-// add one count per active lane to h[digit]
+// Adds one count per active lane to h[digit]. When every active lane of the
+// wave has the same digit (all-equal or sorted rows) the wave adds them with one
+// atomic; when the first active lane's digit is shared by at least 16 lanes that
+// group is added with one atomic and the rest one by one; otherwise every lane
+// adds its own count (distinct digits do not serialise).
 __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t digit) {
   const uint64_t m = ballot(act);
   if (m == 0) return;
   const int leader = __builtin_ctzll(m);
   const uint32_t d0 = readlane<uint32_t>(digit, leader);
-  const bool same = act && digit == d0;
-  const uint64_t sm = ballot(same);
-  if (lane_id() == leader) atomicAdd(&h[d0], popc64(sm));
-  if (act && !same) atomicAdd(&h[digit], 1u);
+  const uint64_t same = ballot(act && digit == d0);
+  const uint32_t ns = popc64(same);
+  if (ns >= 16) {
+    if (lane_id() == leader) atomicAdd(&h[d0], ns);
+    if (same != m && act && digit != d0) atomicAdd(&h[digit], 1u);
+  } else if (act) {
+    atomicAdd(&h[digit], 1u);
+  }
 }
 
 // Exclusive scan, in place, of a[0..E) and b[0..E) by wave 0; totals to *ta, *tb.
@@ -149,13 +169,57 @@ __device__ __forceinline__ void wave0_scan2(uint32_t* a, uint32_t* b, uint32_t* 
   }
 }
 
-// Select the top-K of row[0..n) into ids_out[0..K); *count_out = number selected.
-// row[0..cap) may be read (cap >= n).
-// All NT threads of the workgroup must call this together.
+// Counts, for element i of keys[0..m) (LDS, zero-padded to a multiple of 4),
+//   gt = #{j : keys[j] > keys[i]}  and  tie = #{j < i : keys[j] == keys[i]}
+//   (or, with TIES_ALL, eq = #{j : keys[j] == keys[i]}).
+// Four adjacent lanes share one element, each counting a quarter of the groups
+// of 4 keys, and their counts are summed across the quad; every loop is uniform
+// across the wave. fn(i, key_i, gt, tie_or_eq) is called by the quad's first lane.
+template <int NT, bool TIES_ALL, typename Fn>
+__device__ __forceinline__ void quad_rank(const uint32_t* keys, int m, Fn fn) {
+  const int t = threadIdx.x;
+  const int part = t & 3;
+  const int ng = (m + 3) / 4;
+  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+  for (int i0 = 0; i0 < m; i0 += NT / 4) {
+    const int i = i0 + (t >> 2);
+    const uint32_t ki = i < m ? keys[i] : 0xFFFFFFFFu;
+    uint32_t gt = 0, tie = 0;
+    // groups part, part+4, ...: four groups are read before any is compared
+    for (int g0 = 0; g0 < ng; g0 += 16) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + 4 * u + part;
+        v[u] = k4[g < ng ? g : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + 4 * u + part;
+        if (g < ng) {
+          const uint32_t kv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            gt += kv[c] > ki ? 1u : 0u;
+            tie += (kv[c] == ki && (TIES_ALL || 4 * g + c < i)) ? 1u : 0u;
+          }
+        }
+      }
+    }
+    gt += dpp_u32<kDppQuadXor1>(gt);
+    gt += dpp_u32<kDppQuadXor2>(gt);
+    tie += dpp_u32<kDppQuadXor1>(tie);
+    tie += dpp_u32<kDppQuadXor2>(tie);
+    if (part == 0 && i < m) fn(i, ki, gt, tie);
+  }
+}
+
+// stage_zero (may be null): the row is returned to zero at the end.
 template <int NT, int SLOTS, bool SORTED, bool COHERENT = false>
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
                                                          int32_t* ids_out, int32_t* count_out,
-                                                         SelectSmem<NT, SLOTS, SORTED>& sm) {
+                                                         SelectSmem<NT, SLOTS, SORTED>& sm,
+                                                         float* stage_zero = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
   constexpr int E = SLOTS * NW;
@@ -172,7 +236,6 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   if (cached) load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
 
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
-  if (t == 0) sm.n_in_bin = 0u;
   __syncthreads();
 
   // Each pass histograms the next digit of the keys that still match the
@@ -241,65 +304,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     prefix = (prefix << (p == 2 ? 10 : 11)) | sm.sel_bin;
     need = sm.sel_need;
     level = p + 1;
-    const uint32_t in_bin = sm.sel_tot;
-    if (in_bin == need) break;  // the whole bin is taken: nothing left to resolve
-    if (p == 0 && in_bin <= (uint32_t)kCandCap && ntiles <= 1) {
-      // Few keys share the threshold bin: gather them in LDS and find the
-      // need-th largest directly by counting, instead of two more passes.
-      uint32_t cnt[SLOTS * 4], tot = 0;
-#pragma unroll
-      for (int i = 0; i < SLOTS; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t key = keys[i][j];
-          const uint64_t m = slot_live(0, i) ? ballot(key != kKeyNegInf && (key >> 21) == prefix)
-                                             : 0ull;
-          cnt[i * 4 + j] = (uint32_t)(m != 0);  // reuse: 1 if any lane of the wave is in the bin
-          tot += popc64(m);
-        }
-      }
-      uint32_t base = 0;
-      if (tot != 0) {
-        if (lane == 0) base = atomicAdd(&sm.n_in_bin, tot);
-        base = readlane<uint32_t>(base, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < SLOTS; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (cnt[i * 4 + j] == 0u) continue;
-          const uint32_t key = keys[i][j];
-          const bool inb = key != kKeyNegInf && (key >> 21) == prefix;
-          const uint64_t m = ballot(inb);
-          if (inb) sm.cand[base + mbcnt(m)] = key;
-          base += popc64(m);
-        }
-      }
-      if (t < 4) sm.cand[in_bin + t] = 0u;  // padding: 0 is below every key
-      __syncthreads();
-      // the need-th largest candidate key T, and how many keys equal to T to take
-      const uint4* c4 = reinterpret_cast<const uint4*>(sm.cand);
-      for (int i = t; i < (int)in_bin; i += NT) {
-        const uint32_t ki = sm.cand[i];
-        uint32_t gt = 0, ge = 0;
-        const int ng = (int)(in_bin + 3) / 4;
-#pragma unroll 8
-        for (int j = 0; j < ng; ++j) {
-          const uint4 v = c4[j];
-          gt += (v.x > ki) + (v.y > ki) + (v.z > ki) + (v.w > ki);
-          ge += (v.x >= ki) + (v.y >= ki) + (v.z >= ki) + (v.w >= ki);
-        }
-        if (gt < need && need <= ge) {  // every candidate equal to T writes the same
-          sm.thr_key = ki;
-          sm.thr_need = need - gt;
-        }
-      }
-      __syncthreads();
-      prefix = sm.thr_key;
-      need = sm.thr_need;
-      level = kPasses;
-      break;
-    }
+    if (sm.sel_tot == need) break;  // the whole bin is taken: nothing left to resolve
   }
 
   // ---- emit --------------------------------------------------------------------------
@@ -380,33 +385,13 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     __syncthreads();
     // rank of pair i = number of pairs with a larger key, or an equal key and a
     // smaller id (pairs are stored in ascending id order)
-    const uint4* k4 = reinterpret_cast<const uint4*>(sm.skey);
-    for (int i = t; i < (int)m_out; i += NT) {
-      const uint32_t ki = sm.skey[i];
-      uint32_t r = 0;
-      const int full = i / 4;  // groups entirely below i: ties count
-#pragma unroll 8
-      for (int j = 0; j < full; ++j) {
-        const uint4 v = k4[j];
-        r += (v.x >= ki) + (v.y >= ki) + (v.z >= ki) + (v.w >= ki);
-      }
-      {
-        const uint4 v = k4[full];  // the group holding i
-        const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = full * 4 + c;
-          r += (kv[c] > ki || (kv[c] == ki && j < i)) ? 1u : 0u;
-        }
-      }
-      const int ng = (int)(m_out + 3) / 4;
-#pragma unroll 8
-      for (int j = full + 1; j < ng; ++j) {
-        const uint4 v = k4[j];
-        r += (v.x > ki) + (v.y > ki) + (v.z > ki) + (v.w > ki);
-      }
-      ids_out[r] = sm.sid[i];
-    }
+    quad_rank<NT, false>(sm.skey, (int)m_out, [&](int i, uint32_t, uint32_t gt, uint32_t tie) {
+      ids_out[gt + tie] = sm.sid[i];
+    });
+  }
+  if (stage_zero != nullptr) {
+    if (!cached) __syncthreads();  // streamed rows: every read of the row is done
+    for (int i = t; i < n; i += NT) stage_zero[i] = 0.f;
   }
 }
 

@@ -34,8 +34,7 @@
  *   - bf16 data is passed as raw 16-bit patterns (uint16_t storage).
  *   - Workspace: a caller-owned device buffer of at least the size the
  *     matching *_workspace_bytes() returns. An idx_select workspace must be
- *     zero-filled once before its first use (its counter area is then returned
- *     to zero by every call). One workspace may serve any sequence of calls on
+ *     zero-filled once before its first use (every call returns it to zero). One workspace may serve any sequence of calls on
  *     one stream; calls that may overlap (other streams) need distinct
  *     workspaces.
  */
@@ -128,10 +127,9 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
  * K >= 1 (K <= IDX_MAX_SORTED_K with IDX_SORTED).
  * B <= IDX_MAX_REQUESTS.
  * ws / ws_bytes: workspace of at least idx_workspace_bytes(B, N_pad, H, K, flags)
- * bytes, zero-filled before first use. Its first 64 KiB hold one arrival
- * counter per request, which every call returns to zero; the rest stages the
- * scores. The counter area has a fixed place, so one workspace may serve calls
- * of any shape that fits it.
+ * bytes, zero-filled before first use: 2 MiB of per-request arrival counters
+ * (one 128-byte line each) and staging for the scores. Every call returns the whole workspace to zero,
+ * so one workspace may serve calls of any shape that fits it.
  */
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags);
 int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,

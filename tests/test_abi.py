@@ -55,9 +55,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # a fixed 64 KiB of arrival counters, then B rows of round_up(N_pad, 4) floats
-    assert lib.idx_workspace_bytes(4, 8192, 4, 256, 0) == 65536 + 4 * 8192 * 4
-    assert lib.idx_workspace_bytes(1, 1001, 4, 8, 0) == 65536 + 1004 * 4
+    # 2 MiB of arrival counters (128 B each), then B rows of round_up(N_pad, 4) floats
+    assert lib.idx_workspace_bytes(4, 8192, 4, 256, 0) == (2 << 20) + 4 * 8192 * 4
+    assert lib.idx_workspace_bytes(1, 1001, 4, 8, 0) == (2 << 20) + 1004 * 4
     assert lib.idx_workspace_bytes(0, 10, 4, 8, 0) == 0
     assert lib.idx_assign_workspace_bytes(1024, 128) == 4096
     assert lib.idx_assign_workspace_bytes(1, 128) == 256
