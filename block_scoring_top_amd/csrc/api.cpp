@@ -137,10 +137,12 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
                                         tickets, stage, stage_stride(N_pad), stream));
 }
 
+// -|c|^2/2 per centroid, padded with -inf to a multiple of 128 (a whole number of
+// centroid tiles)
 size_t idx_assign_workspace_bytes(int C, int D) {
   (void)D;
   if (C < 1) return 0;
-  return round_up((size_t)C * sizeof(float), 256);
+  return round_up(round_up((size_t)C, 128) * sizeof(float), 256);
 }
 
 int idx_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C, int D,

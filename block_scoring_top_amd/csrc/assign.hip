@@ -5,16 +5,18 @@
 //   assign[i] = argmax_j ( x_i . c_j - |c_j|^2 / 2 ),  ties to the lower j,
 //
 // which has the same maximiser as 2 x.c - |c|^2. The contraction X . C^T is a
-// dense bf16 GEMM with fp32 accumulation, so it runs on v_mfma_f32_32x32x16_bf16;
-// the bias -|c|^2/2 is loaded into the accumulators before the products are
-// added, and the argmax is a running max in registers, so the score matrix is
-// never written anywhere.
+// dense bf16 GEMM with fp32 accumulation, so it runs on v_mfma_f32_32x32x16_bf16.
+// The bias -|c|^2/2 (computed once per call by a small kernel into the
+// workspace) is loaded into the accumulators before the products are added, and
+// the argmax is a running max in registers: the score matrix is never written.
 //
-// Layout: the MFMA's A operand is a 32-centroid x 16-dim slice of C (from LDS),
-// the B operand a 16-dim x 32-point slice of X^T (registers, loaded once). The
-// 32x32 result tile then has one point per lane column (lane % 32) and 16
-// centroid rows per lane, so the max over centroids is mostly in-lane; lanes l
-// and l^32 hold disjoint centroid rows of the same point and are merged once.
+// Layout: the MFMA's A operand is a 32-centroid x 16-dim slice of C (from a
+// double-buffered LDS tile of 64 centroids, filled by direct-to-LDS loads that
+// overlap the previous tile's products), the B operand a 16-dim x 32-point
+// slice of X^T (registers, loaded once). The 32x32 result tile then has one
+// point per lane column (lane % 32) and 16 centroid rows per lane, so the max
+// over centroids is mostly in-lane; lanes l and l^32 hold disjoint centroid rows
+// of the same point and are merged once at the end.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -29,46 +31,73 @@ constexpr int kAsgNT = 256;          // 4 waves
 constexpr int kAsgPtsPerWave = 64;   // two 32-point column blocks
 constexpr int kAsgPts = kAsgPtsPerWave * (kAsgNT / kWave);
 constexpr int kAsgTileC = 64;        // centroids per LDS tile: two 32-row blocks
-constexpr int kChunks = kHeadDim * 2 / 16;  // 16-byte chunks per bf16 row (16)
+constexpr int kChunks = kHeadDim * 2 / 16;                // 16-byte chunks per bf16 row (16)
+constexpr int kTileLoads = kAsgTileC * kChunks / kAsgNT;  // 16-byte loads per thread per tile
 
-// -|c_j|^2 / 2 in fp32 (squares of bf16 values are exact in fp32)
+// -|c_j|^2 / 2 in fp32, once per call (squares of bf16 values are exact in fp32),
+// padded with -inf up to a whole number of centroid tiles
 __global__ __launch_bounds__(256) void cnorm_kernel(const uint16_t* __restrict__ c, int C,
                                                     float* __restrict__ cn) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int l16 = lane & 15;
+  const int l16 = threadIdx.x & 15;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (row >= C) return;
-  const uint4 v = reinterpret_cast<const uint4*>(c + (size_t)row * kHeadDim)[l16];
+  const int rows = (C + kAsgTileC - 1) / kAsgTileC * kAsgTileC;
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const uint4 v = reinterpret_cast<const uint4*>(c + (size_t)(row < C ? row : C - 1) * kHeadDim)[l16];
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
   float s = 0.f;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
+    const float a = bf16_lo(wd[k]), b = bf16_hi(wd[k]);
     s = fmaf(a, a, s);
     s = fmaf(b, b, s);
   }
   s = sum16(s);
-  if (l16 == 0) cn[row] = -0.5f * s;
+  if (l16 == 0) cn[row] = row < C ? -0.5f * s : -__builtin_inff();
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// row r of a centroid tile: its 16-byte chunk k sits at chunk position k ^ (r & 15)
+// row r of a centroid tile: its 16-byte chunk k sits at chunk position k ^ (r & 15),
+// so the 32 lanes reading one chunk column of 32 rows hit distinct banks
 __device__ __forceinline__ int swz(int r, int k) { return r * kChunks + (k ^ (r & 15)); }
 
-__global__ __launch_bounds__(kAsgNT) void assign_kernel(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ c,
-                                                        const float* __restrict__ cn,
-                                                        int32_t* __restrict__ assign,
-                                                        float* __restrict__ best_out, int64_t N,
-                                                        int C) {
-  __shared__ uint4 ctile[kAsgTileC * kChunks];  // 16 KiB
-  __shared__ float ctn[kAsgTileC];
+// Global -> LDS without a trip through registers (16-byte direct-to-LDS loads).
+// Load i of wave w fills the 64 consecutive 16-byte LDS slots p = 64 (4w + i) +
+// lane; slot p holds chunk (p & 15) ^ (row & 15) of tile row p >> 4, which is
+// the swizzled layout the MFMA operand reads expect. Rows past C repeat row C-1
+// (their bias is -inf, so they never win). Wave w < kAsgTileC/64 also brings 64
+// of the tile's biases from the -inf-padded norm buffer.
+__device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
+                                               const float* __restrict__ cn, int C, int j0,
+                                               uint4* tile, float* tn) {
+  const int t = threadIdx.x;
+  const int w = t >> 6, lane = t & (kWave - 1);
+#pragma unroll
+  for (int i = 0; i < kTileLoads; ++i) {
+    const int slot0 = (w * kTileLoads + i) * kWave;  // wave-uniform LDS base
+    const int p = slot0 + lane;
+    const int row = p >> 4;
+    const int k = (p & 15) ^ (row & 15);
+    const int j = j0 + row < C ? j0 + row : C - 1;
+    __builtin_amdgcn_global_load_lds(c + (size_t)j * kHeadDim + k * 8, tile + slot0, 16, 0, 0);
+  }
+  if (w < kAsgTileC / kWave)
+    __builtin_amdgcn_global_load_lds(cn + j0 + w * kWave + lane, tn + w * kWave, 4, 0, 0);
+}
+
+__global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ c,
+                                                           const float* __restrict__ cn,
+                                                           int32_t* __restrict__ assign,
+                                                           float* __restrict__ best_out,
+                                                           int64_t N, int C) {
+  __shared__ uint4 ctile[2][kAsgTileC * kChunks];  // 2 x 16 KiB
+  __shared__ float4 ctn4[2][kAsgTileC / 4];
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
-  const int col = lane & 31;  // point within a 32-point block; centroid row for A
-  const int half = lane >> 5; // which 8 dims of a 16-dim k-step this lane carries
+  const int col = lane & 31;   // point within a 32-point block; centroid row for A
+  const int half = lane >> 5;  // which 8 dims of a 16-dim k-step this lane carries
   const int64_t p0 = (int64_t)blockIdx.x * kAsgPts + w * kAsgPtsPerWave;
 
   // B operand: this lane's point rows, all 128 dims, as 8 k-steps of 8 bf16
@@ -85,56 +114,72 @@ __global__ __launch_bounds__(kAsgNT) void assign_kernel(const uint16_t* __restri
   float best[2] = {-__builtin_inff(), -__builtin_inff()};
   int bidx[2] = {0, 0};
 
-  for (int j0 = 0; j0 < C; j0 += kAsgTileC) {
-    __syncthreads();  // the previous tile is no longer read
-#pragma unroll
-    for (int i = 0; i < kAsgTileC * kChunks / kAsgNT; ++i) {
-      const int g = t + i * kAsgNT;
-      const int r = g / kChunks, k = g % kChunks;
-      const int j = j0 + r < C ? j0 + r : C - 1;  // clamp; rows past C are never winners
-      ctile[swz(r, k)] = reinterpret_cast<const uint4*>(c + (size_t)j * kHeadDim)[k];
-    }
-    if (t < kAsgTileC) ctn[t] = (j0 + t < C) ? cn[j0 + t] : -__builtin_inff();
-    __syncthreads();
+  const int ntiles = (C + kAsgTileC - 1) / kAsgTileC;
+  load_ctile_lds(c, cn, C, 0, ctile[0], reinterpret_cast<float*>(ctn4[0]));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int j0 = tile * kAsgTileC;
+    // the next tile streams into the idle buffer while this one is multiplied
+    if (tile + 1 < ntiles)
+      load_ctile_lds(c, cn, C, j0 + kAsgTileC, ctile[buf ^ 1],
+                     reinterpret_cast<float*>(ctn4[buf ^ 1]));
+
+    // four independent accumulator chains (2 centroid blocks x 2 point blocks)
+    // keep the matrix pipeline busy; A fragments are read one k-step ahead of use
     f32x16 acc[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float bias = ctn[rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
-        acc[rb][0][r] = bias;
-        acc[rb][1][r] = bias;
+      for (int g = 0; g < 4; ++g) {  // rows 8g + 4*half + 0..3 of a 32-row block
+        const float4 bias = ctn4[buf][rb * 8 + 2 * g + half];
+        acc[rb][0][4 * g + 0] = acc[rb][1][4 * g + 0] = bias.x;
+        acc[rb][0][4 * g + 1] = acc[rb][1][4 * g + 1] = bias.y;
+        acc[rb][0][4 * g + 2] = acc[rb][1][4 * g + 2] = bias.z;
+        acc[rb][0][4 * g + 3] = acc[rb][1][4 * g + 3] = bias.w;
       }
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 a = as_bf16x8(ctile[swz(rb * 32 + col, 2 * ks + half)]);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(xb[cb][ks]),
-                                                               acc[rb][cb], 0, 0, 0);
-      }
+      const bf16x8 a0 = as_bf16x8(ctile[buf][swz(col, 2 * ks + half)]);
+      const bf16x8 a1 = as_bf16x8(ctile[buf][swz(32 + col, 2 * ks + half)]);
+      const bf16x8 b0 = as_bf16x8(xb[0][ks]), b1 = as_bf16x8(xb[1][ks]);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
     }
-    // running argmax; centroid index increases with (rb, r) for a fixed lane, so
-    // a strict comparison keeps the lowest index among equal values
+    // Running argmax. The 16 values of a lane are reduced with 3-input maxes;
+    // only when some lane of the wave finds a strictly larger value is the index
+    // of its first (lowest-index) occurrence searched. For a fixed lane the
+    // centroid index increases with (tile, rb, r), so strict comparisons keep
+    // the lowest index among equal values.
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int cb = 0; cb < 2; ++cb) {
+        const f32x16& v = acc[rb][cb];
+        float m = v[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = acc[rb][cb][r];
-          const int j = j0 + rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (v > best[cb]) {
-            best[cb] = v;
-            bidx[cb] = j;
+        for (int r = 1; r < 15; r += 2)  // a chain of 3-input maxes
+          m = __builtin_fmaxf(__builtin_fmaxf(m, v[r]), v[r + 1]);
+        m = __builtin_fmaxf(m, v[15]);
+        const bool better = m > best[cb];
+        if (__builtin_amdgcn_ballot_w64(better) != 0) {
+          int rr = 15;
+#pragma unroll
+          for (int r = 14; r >= 0; --r) rr = (v[r] == m) ? r : rr;
+          if (better) {
+            best[cb] = m;
+            bidx[cb] = j0 + rb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
           }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
+    __syncthreads();                 // ... and every wave's; this buffer is free again
   }
 
   // merge the two lanes that share a point (l and l^32)
@@ -157,9 +202,10 @@ __global__ __launch_bounds__(kAsgNT) void assign_kernel(const uint16_t* __restri
 int launch_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C,
                   float* cnorm, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(cnorm_kernel, dim3((unsigned)((C + 15) / 16)), dim3(256), 0, s,
+  const int rows = (C + kAsgTileC - 1) / kAsgTileC * kAsgTileC;
+  hipLaunchKernelGGL(cnorm_kernel, dim3((unsigned)(rows / 16)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(c), C, cnorm);
-  int e = (int)hipGetLastError();
+  const int e = (int)hipGetLastError();
   if (e != 0) return e;
   const int64_t nblk = (N + kAsgPts - 1) / kAsgPts;
   hipLaunchKernelGGL(assign_kernel, dim3((unsigned)nblk), dim3(kAsgNT), 0, s,

@@ -60,7 +60,8 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(1, 1001, 4, 8, 0) == (2 << 20) + 1004 * 4
     assert lib.idx_workspace_bytes(0, 10, 4, 8, 0) == 0
     assert lib.idx_assign_workspace_bytes(1024, 128) == 4096
-    assert lib.idx_assign_workspace_bytes(1, 128) == 256
+    assert lib.idx_assign_workspace_bytes(1, 128) == 512
+    assert lib.idx_assign_workspace_bytes(1031, 128) == 1152 * 4
 
 
 def score_call(lib, **kw):
