@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
 }
 
 // ---- idx_topk ----------------------------------------------------------------------------
-template <bool SORTED>
+template <bool SORTED, bool BLOCKED>
 __global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ n_valid,
                                                        int32_t* __restrict__ ids,
@@ -48,13 +48,13 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<kTopkNT, kTopkSlots, SORTED>(scores + (size_t)b * N, n, N, K, ids + (size_t)b * K,
+  select_row<kTopkNT, kTopkSlots, SORTED, false, BLOCKED>(scores + (size_t)b * N, n, N, K, ids + (size_t)b * K,
                                           counts ? counts + b : nullptr, sm);
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
 // NT threads per workgroup, select tile NT*SLOTS*4 keys.
-template <bool BF16, bool SORTED, int NT, int SLOTS>
+template <bool BF16, bool SORTED, int NT, int SLOTS, bool BLOCKED>
 __global__ __launch_bounds__(NT) void select_fused_kernel(
     const void* __restrict__ q, const void* __restrict__ c, const int32_t* __restrict__ seq_len,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, float* __restrict__ scores_out,
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   if (threadIdx.x == 0)  // ready for the next call on this workspace
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  select_row<NT, SLOTS, SORTED, true>(row, nv, row_cap, K, ids + (size_t)b * K,
+  select_row<NT, SLOTS, SORTED, true, BLOCKED>(row, nv, row_cap, K, ids + (size_t)b * K,
                                       counts ? counts + b : nullptr, sm,
                                       scores_out != nullptr ? nullptr : row);
 }
@@ -124,10 +124,15 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
                 int B, int N, int K, bool sorted, void* stream) {
   const dim3 grid((unsigned)B), block(kTopkNT);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Rows come from HBM here, so they are read in the striped layout (every load
+  // fully coalesced); the blocked layout's strided loads cost more than its
+  // cheaper emit saves.
   if (sorted)
-    hipLaunchKernelGGL(topk_kernel<true>, grid, block, 0, s, scores, n_valid, ids, counts, N, K);
+    hipLaunchKernelGGL((topk_kernel<true, false>), grid, block, 0, s, scores, n_valid, ids,
+                       counts, N, K);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, grid, block, 0, s, scores, n_valid, ids, counts, N, K);
+    hipLaunchKernelGGL((topk_kernel<false, false>), grid, block, 0, s, scores, n_valid, ids,
+                       counts, N, K);
   return (int)hipGetLastError();
 }
 
@@ -140,12 +145,23 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   // wide: 1024-thread workgroups (16 waves keep the selecting workgroup's SIMDs
   // busy; for a few long requests); otherwise 256 threads (many requests)
-#define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_)                                                     \
-  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_>), grid, dim3(NT_), 0, s, q, c,     \
+  // blocked: every row fits the select's register tile (1024*2*4 = 256*8*4 = 8192;
+  // 256-thread workgroups use 2 slots, 256*2*4 = 2048, when that is enough)
+  const bool blocked = N_pad <= 8192;
+  const bool short_rows = N_pad <= 2048;
+#define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_, BL)                                                 \
+  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL>), grid, dim3(NT_), 0, s, q, c, \
                      seq_len, ids, counts, scores_out, H, N_pad, page_size, K, chunk, nchunk,  \
                      tickets, stage, stage_stride)
-#define IDX_LAUNCH_FUSED_NT(BF, SO) \
-  if (wide) IDX_LAUNCH_FUSED(BF, SO, 1024, 2); else IDX_LAUNCH_FUSED(BF, SO, 256, 8)
+#define IDX_LAUNCH_FUSED_NT(BF, SO)                                                  \
+  if (wide) {                                                                        \
+    if (blocked) IDX_LAUNCH_FUSED(BF, SO, 1024, 2, true);                            \
+    else IDX_LAUNCH_FUSED(BF, SO, 1024, 2, false);                                   \
+  } else {                                                                           \
+    if (short_rows) IDX_LAUNCH_FUSED(BF, SO, 256, 2, true);                          \
+    else if (blocked) IDX_LAUNCH_FUSED(BF, SO, 256, 8, true);                        \
+    else IDX_LAUNCH_FUSED(BF, SO, 256, 8, false);                                    \
+  }
   if (bf16) {
     if (sorted) { IDX_LAUNCH_FUSED_NT(true, true); }
     else { IDX_LAUNCH_FUSED_NT(true, false); }

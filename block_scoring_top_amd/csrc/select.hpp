@@ -42,6 +42,7 @@ struct SelectSmem {
   static constexpr int E = SLOTS * NW;  // emit-count entries per tile
   uint32_t hist[2][kBins];
   uint32_t wsum[4];
+  uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
   uint32_t sel_bin, sel_need, sel_tot, n_cand;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
@@ -113,6 +114,59 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int cap, int 
     for (int j = 0; j < 4; ++j) {
       const int e = base + (i * NT + t) * 4 + j;
       keys[i][j] = e < n ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+    }
+  }
+}
+
+// Loads a whole row (n <= NT * SLOTS * 4) in the blocked layout: thread t holds
+// the kpt4 consecutive entries starting at t * kpt4 (kpt4 a multiple of 4, the
+// same for every thread), so its keys are in ascending index order. Entries at
+// or past n become kKeyNegInf. Loads are issued before any is used.
+template <int NT, int SLOTS, bool COHERENT>
+__device__ __forceinline__ void load_keys_blocked(const float* row, int n, int cap, int kpt4,
+                                                  uint32_t (&keys)[SLOTS][4]) {
+  const int t = threadIdx.x;
+  const int e_base = t * kpt4;
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(row);
+  const bool aligned4 = (((uintptr_t)row & 15) == 0) && (cap & 3) == 0;
+  if (aligned4) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, cap * 4, kBufferDword3);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (4 * i < kpt4) {  // uniform
+        // buffer loads: bounds-checked (zeros past cap); sc1 when the row was
+        // written by other workgroups in this kernel
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (e_base + 4 * i) * 4, 0,
+                                                             COHERENT ? kCachePolicySc1 : 0);
+        keys[i][0] = v[0];
+        keys[i][1] = v[1];
+        keys[i][2] = v[2];
+        keys[i][3] = v[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (4 * i < kpt4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = e_base + 4 * i + j;
+          if constexpr (COHERENT)
+            keys[i][j] = __hip_atomic_load(const_cast<uint32_t*>(bits) + (e < n ? e : 0),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            keys[i][j] = bits[e < n ? e : 0];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e_base + 4 * i + j;
+      keys[i][j] = (4 * i < kpt4 && e < n) ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
     }
   }
 }
@@ -215,7 +269,10 @@ __device__ __forceinline__ void quad_rank(const uint32_t* keys, int m, Fn fn) {
 }
 
 // stage_zero (may be null): the row is returned to zero at the end.
-template <int NT, int SLOTS, bool SORTED, bool COHERENT = false>
+// BLOCKED: the caller guarantees n <= NT * SLOTS * 4; the row is held in the
+// blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
+// when it does not fit one register tile).
+template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED>
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
                                                          int32_t* ids_out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS, SORTED>& sm,
@@ -227,13 +284,20 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
-  const int ntiles = (n + TILE - 1) / TILE;
+  const int ntiles = BLOCKED ? 1 : (n + TILE - 1) / TILE;
   const bool cached = ntiles <= 1;
-  // slots of a tile that hold no entry of the row, for any thread, are skipped
-  auto slot_live = [&](int base, int i) { return base + i * NT * 4 < n; };
+  // blocked layout: thread t owns kpt4 consecutive entries
+  const int kpt4 = BLOCKED ? ((n + NT - 1) / NT + 3) / 4 * 4 : 0;
+  // slots that hold no entry of the row, for any thread, are skipped
+  auto slot_live = [&](int base, int i) {
+    return BLOCKED ? 4 * i < kpt4 : base + i * NT * 4 < n;
+  };
 
   uint32_t keys[SLOTS][4];
-  if (cached) load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
+  if constexpr (BLOCKED)
+    load_keys_blocked<NT, SLOTS, COHERENT>(row, n, cap, kpt4, keys);
+  else if (cached)
+    load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
 
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
   __syncthreads();
@@ -310,8 +374,59 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   // ---- emit --------------------------------------------------------------------------
   const int shiftL = take_all ? 0 : (level == 1 ? 21 : (level == 2 ? 10 : 0));
   const uint32_t m_out = take_all ? ncand : (uint32_t)K;
+  auto classify = [&](uint32_t key, bool& gt, bool& eq) {
+    const bool act = key != kKeyNegInf;
+    const uint32_t hi = take_all ? 0u : (key >> shiftL);
+    gt = act && (take_all || hi > prefix);
+    eq = act && !take_all && hi == prefix;
+  };
+  if constexpr (BLOCKED) {
+    // Blocked layout: each thread counts its taken-for-sure (gt) and threshold
+    // (eq) keys, one workgroup scan of the packed counts (eq << 16 | gt; both
+    // fit 16 bits since n <= 32768) gives the keys before the thread, and the
+    // thread then writes its taken ids in ascending order.
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (!slot_live(0, i)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bool gt, eq;
+        classify(keys[i][j], gt, eq);
+        packed += (gt ? 1u : 0u) + (eq ? 0x10000u : 0u);
+      }
+    }
+    const uint32_t incl = wave_incl_scan(packed);
+    if (lane == kWave - 1) sm.wpack[w] = incl;
+    __syncthreads();
+    uint32_t before = incl - packed;
+    for (int ww = 0; ww < w; ++ww) before += sm.wpack[ww];
+    uint32_t gb = before & 0xFFFFu, eb = before >> 16;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (!slot_live(0, i)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bool gt, eq;
+        classify(keys[i][j], gt, eq);
+        const bool take = gt || (eq && eb < need);
+        const uint32_t pos = gb + (eb < need ? eb : need);
+        if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
+          const int id = t * kpt4 + 4 * i + j;
+          if constexpr (SORTED) {
+            sm.skey[pos] = keys[i][j];
+            sm.sid[pos] = id;
+          } else {
+            ids_out[pos] = id;
+          }
+        }
+        gb += gt ? 1u : 0u;
+        eb += eq ? 1u : 0u;
+      }
+    }
+  }
   uint32_t carry_gt = 0, carry_eq = 0;
-  for (int tile = 0; tile < ntiles; ++tile) {
+  for (int tile = 0; tile < (BLOCKED ? 0 : ntiles); ++tile) {
     if (!cached) {
       __syncthreads();  // the previous tile's counts have been read
       load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);

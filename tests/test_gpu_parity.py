@@ -110,6 +110,16 @@ def test_select_many_requests(chunk_log2):
     full_select_check(x, 100, True, chunk_log2)
 
 
+def test_select_many_requests_medium_rows():
+    """More than 32 requests, tables between 2048 and 8192 blocks (8 key slots)."""
+    rng = np.random.default_rng(311)
+    seq = rng.integers(0, 5000 * 16, 36)
+    seq[:2] = [5000 * 16, 2049 * 16]
+    x = synth.make_indexer(36, 4, 128, 5000, seq, 700, "bf16", 311)
+    full_select_check(x, 700, False)
+    full_select_check(x, 700, True)
+
+
 def test_select_many_requests_multi_tile():
     """More than 32 requests with rows longer than one 8192-key register tile."""
     x = synth.make_indexer(33, 2, 128, 9000, [9000 * 16] * 30 + [8193 * 16, 5, 8192 * 16],
