@@ -280,6 +280,12 @@ def parse_pmc(dirs, out_path, workload):
     with open(out_path, "w") as f:
         f.write(f"# HBM traffic of {kern} (workload {workload}) from rocprofv3 --pmc\n")
         f.write("# byte counters scaled by (1 GiB) / (counter for a plain 1 GiB device copy)\n")
+        f.write("# commands (run from /tmp, repository at /root/repo):\n")
+        for ctr, d in zip(("FETCH_SIZE", "WRITE_SIZE"), dirs):
+            f.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d /root/repo/{d} -o pmc -- "
+                    f"python3 /root/repo/bench.py --workload {workload} --steps 20 --warmup 5 "
+                    "--no-cpu-baseline --no-graph --pmc-calibrate\n")
+        f.write(f"#   python3 bench.py --workload {workload} --parse-pmc {' '.join(dirs)}\n")
         for k_, v in res.items():
             f.write(f"{k_}={v}\n")
     print(json.dumps(res))

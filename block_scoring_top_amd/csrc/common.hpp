@@ -90,6 +90,20 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// min / max over the 64 lanes of a wave (returned in every lane)
+template <bool IS_MIN>
+__device__ __forceinline__ uint32_t wave_reduce_minmax(uint32_t v) {
+  const int ident = IS_MIN ? -1 : 0;  // lanes without a source keep the identity
+  auto op = [](uint32_t a, uint32_t b) { return IS_MIN ? (a < b ? a : b) : (a > b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowShr1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowShr1 + 1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowShr1 + 3, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowShr1 + 7, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // sum over groups of 16 consecutive lanes; every lane of a group gets the same
 // value (the pairings are symmetric, so each lane adds the same operands)
 __device__ __forceinline__ float sum16(float v) {

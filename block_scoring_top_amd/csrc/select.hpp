@@ -43,6 +43,7 @@ struct SelectSmem {
   uint32_t hist[2][kBins];
   uint32_t wsum[4];
   uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
+  uint32_t wmin[NW], wmax[NW];  // per-wave min / max of a pass's active keys
   uint32_t sel_bin, sel_need, sel_tot, n_cand;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
@@ -314,6 +315,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     const int shift = digit_shift(p);
     const uint32_t dmask = digit_mask(p);
     const int hshift = p == 0 ? 0 : digit_shift(p - 1);  // the resolved bits sit above this
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // over this pass's active keys
     for (int tile = 0; tile < ntiles; ++tile) {
       if (!cached) load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
 #pragma unroll
@@ -324,10 +326,23 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           const uint32_t key = keys[i][j];
           const bool act = key != kKeyNegInf && (p == 0 || (key >> hshift) == prefix);
           hist_add(h, act, (key >> shift) & dmask);
+          kmin = act && key < kmin ? key : kmin;
+          kmax = act && key > kmax ? key : kmax;
         }
       }
     }
+    kmin = wave_reduce_minmax<true>(kmin);
+    kmax = wave_reduce_minmax<false>(kmax);
+    if (lane == 0) {
+      sm.wmin[w] = kmin;
+      sm.wmax[w] = kmax;
+    }
     __syncthreads();
+    // read before the next barrier: the next pass rewrites these slots
+    for (int ww = 0; ww < NW; ++ww) {
+      kmin = sm.wmin[ww] < kmin ? sm.wmin[ww] : kmin;
+      kmax = sm.wmax[ww] > kmax ? sm.wmax[ww] : kmax;
+    }
     uint32_t c8[8], loc = 0, incl = 0;
     if (t < 256) {
       const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 8 * (t + 1));
@@ -364,6 +379,13 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         take_all = true;
         break;
       }
+    }
+    // every active key is the same value: the threshold is that key, of which
+    // `need` are taken (identical keys would only fill one bin per later pass)
+    if (kmin == kmax) {
+      prefix = kmin;
+      level = kPasses;
+      break;
     }
     prefix = (prefix << (p == 2 ? 10 : 11)) | sm.sel_bin;
     need = sm.sel_need;
