@@ -17,6 +17,14 @@ Prints one JSON line:
   roofline      the dominant kernel: algorithmic bytes (or flops) per launch /
                 average launch time, against the MI355X peak
   cpu_baseline  the CPU oracle on the host cores, on a bounded sample
+  steady_us_per_call    median / min over five replays of the timed graph
+  cold_us_per_call      32 single calls, each after a 1 GiB overwrite that evicts
+                        L2 and the last-level cache (HIP events around the call)
+  host_e2e_us_per_call  host wall clock of one call plus a stream synchronise
+  sorted_us_per_call    the score-ordered output (workloads 2-4 headline the
+                        id-ordered one)
+  floor                 an empty launch and a streaming read of the same bytes
+                        (alone, and followed by one arrival counter) on this GPU
 
 Other modes:
   --workload N         1..5 (1: tiny fp32, 2: default, 3: top-K stress,
@@ -94,10 +102,14 @@ class Indexer:
         self.alg_bytes = (self.units * self.row_bytes + x.q.size * elem + 4 * x.B + 4 * x.B * x.K)
         self.alg_flops = 2 * self.units * x.D  # after summing the heads once per request
 
-    def step(self, i):
+    def step(self, i, sorted=None):
         q, c, sl = self.inputs[i % len(self.inputs)]
-        self.idx.idx_select(q, c, sl, self.x.K, page_size=self.x.page_size, sorted=self.x.sorted,
+        self.idx.idx_select(q, c, sl, self.x.K, page_size=self.x.page_size,
+                            sorted=self.x.sorted if sorted is None else sorted,
                             ids=self.ids, counts=self.counts, ws=self.ws)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][1]
 
     def describe(self):
         x = self.x
@@ -134,9 +146,12 @@ class Topk:
         self.alg_bytes = B * N * 4 + B * x.K * 4
         self.alg_flops = 0
 
-    def step(self, i):
-        self.idx.idx_topk(self.inputs[i % len(self.inputs)], self.x.K, None, False, ids=self.ids,
-                          counts=self.counts)
+    def step(self, i, sorted=None):
+        self.idx.idx_topk(self.inputs[i % len(self.inputs)], self.x.K, None, bool(sorted),
+                          ids=self.ids, counts=self.counts)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)]
 
     def describe(self):
         B, N = self.x.scores.shape
@@ -172,9 +187,12 @@ class Assign:
         self.alg_bytes = N * D * 2 + C * D * 2 + N * 4
         self.alg_flops = 2 * N * C * D
 
-    def step(self, i):
+    def step(self, i, sorted=None):
         xd, cd = self.inputs[i % len(self.inputs)]
         self.idx.idx_assign(xd, cd, assign=self.assign, ws=self.ws)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][0]
 
     def describe(self):
         N, D = self.x.x.shape
@@ -226,6 +244,94 @@ def blas_threads():
         return max(n) if n else 1
     except Exception:
         return 1
+
+
+# ----------------------------------------------------------------------------------------
+# timing helpers
+# ----------------------------------------------------------------------------------------
+def graph_time(torch, fn, steps, reps=1):
+    """Capture `steps` calls fn(i) into one HIP graph; per-call ms of each of `reps`
+    replays (HIP events on the replaying stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    del g
+    return out
+
+
+def floors(torch, idx, wl, steps):
+    """Attainable floor at this size: an empty launch, and a streaming read of the
+    call's algorithmic bytes (rotating over the input copies, so from HBM), alone
+    and followed by one arrival counter; the read takes the best of a small sweep
+    of launch shapes."""
+    src0 = wl.read_src(0)
+    nbytes = min(wl.alg_bytes, src0.numel() * src0.element_size()) // 16 * 16
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    ticket = torch.zeros(64, dtype=torch.int32, device="cuda")
+    res = {"bytes": nbytes,
+           "empty_us": min(graph_time(torch, lambda i: idx.idx_floor_empty(1), steps, 3)) * 1e3}
+    for key, tk in (("read", None), ("read_handoff", ticket)):
+        best = None
+        for threads in (256, 1024):
+            for blocks in (64, 128, 256, 512, 1024, 2048):
+                t = min(graph_time(torch, lambda i: idx.idx_floor_read(
+                    wl.read_src(i), nbytes, sink, tk, blocks, threads), steps, 3)) * 1e3
+                if best is None or t < best[0]:
+                    best = (t, blocks, threads)
+        res[key + "_us"] = best[0]
+        res[key + "_launch"] = f"{best[1]} x {best[2]}"
+    res["read_GBps"] = nbytes / (res["read_us"] * 1e-6) / 1e9
+    return res
+
+
+def cold_times(torch, wl, n):
+    """Per-call GPU time with L2 and the last-level cache flushed before each call
+    (a 1 GiB buffer is overwritten first)."""
+    flush = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = []
+    for i in range(n):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wl.step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del flush
+    return out
+
+
+def host_e2e_times(torch, wl, n):
+    """Wall clock of one host call plus a stream synchronise."""
+    out = []
+    for i in range(n):
+        t0 = time.perf_counter()
+        wl.step(i)
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) * 1e3)
+    return out
+
+
+def stats_us(ms_list):
+    return {"median": statistics.median(ms_list) * 1e3, "min": min(ms_list) * 1e3,
+            "n": len(ms_list)}
 
 
 # ----------------------------------------------------------------------------------------
@@ -321,6 +427,8 @@ def main():
                     help="time host-launched steps instead of a replayed HIP graph")
     ap.add_argument("--pmc-calibrate", action="store_true")
     ap.add_argument("--parse-pmc", nargs="+", default=None)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the floor, cold, host end-to-end and sorted measurements")
     ap.add_argument("--out", default=None)
     a = ap.parse_args()
 
@@ -405,6 +513,30 @@ def main():
     log(f"[bench] {ms * 1e3:.2f} us per step (events), {wall / a.steps * 1e6:.2f} us wall, "
         f"eager {eager_ms * 1e3:.2f} us per step")
 
+    launch_desc = "eager" if graph is None else f"hipGraph of {a.steps} steps"
+    extras = {}
+    if not a.no_extras:
+        # the same graph replayed again: spread of the steady-state figure
+        if graph is not None:
+            reps = []
+            for _ in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                reps.append(e0.elapsed_time(e1) / a.steps)
+            extras["steady_us_per_call"] = stats_us([ms] + reps)
+        graph = None
+        log("[bench] cold calls, host end-to-end, floors")
+        extras["cold_us_per_call"] = stats_us(cold_times(torch, wl, 32))
+        extras["host_e2e_us_per_call"] = stats_us(host_e2e_times(torch, wl, 32))
+        if a.workload in (2, 3, 4):  # headline unsorted; the score-ordered output beside it
+            extras["sorted_us_per_call"] = min(graph_time(
+                torch, lambda i: wl.step(i, sorted=True), min(a.steps, 1000), 3)) * 1e3
+        extras["floor"] = floors(torch, idx, wl, min(a.steps, 200))
+        log(f"[bench] floors: {json.dumps(extras['floor'])}")
+
     per_s = 1e3 / ms
     if a.workload == 5:
         bound, unit = "mfma", "TFLOP/s"
@@ -421,7 +553,7 @@ def main():
         "unit": {5: "points/s"}.get(a.workload, "entries/s" if a.workload == 3 else "blocks/s"),
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
-        "launch": "eager" if graph is None else f"hipGraph of {a.steps} steps",
+        "launch": launch_desc,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": wl.describe(),
@@ -429,6 +561,9 @@ def main():
                      "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": traffic,
                      "alg_bytes_per_launch": wl.alg_bytes, "alg_flops_per_launch": wl.alg_flops},
     }
+    if a.workload == 5:
+        out["roofline"]["hbm_frac"] = wl.alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    out.update(extras)
     if not a.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle (~{a.cpu_seconds:.0f} s)")
         v, sample = wl.cpu_oracle(a.cpu_seconds)

@@ -15,7 +15,7 @@ import torch
 
 __all__ = ["idx_score", "idx_topk", "idx_select", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
-           "lib_path", "load", "IDX_SORTED", "IdxError"]
+           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libidx.so")
@@ -36,6 +36,8 @@ _SIGS = {
     "idx_assign": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int64, _c_int, _c_int, _c_int, _vp,
                             _c_size, _vp]),
     "idx_status_string": (ctypes.c_char_p, [_c_int]),
+    "idx_floor_empty": (_c_int, [_c_int, _vp]),
+    "idx_floor_read": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _vp]),
 }
 
 _lib = None
@@ -199,3 +201,18 @@ def idx_assign(x, c, return_best=False, assign=None, best=None, ws=None):
     _check("idx_assign", lib.idx_assign(_ptr(x), _ptr(c), _ptr(assign), _ptr(best), N, C, D,
                                         _dtype_code(x), _ptr(ws), ws.numel(), _stream(dev)))
     return assign, best
+
+
+def idx_floor_empty(blocks=1):
+    """One empty launch of `blocks` workgroups (measurement floor)."""
+    _check("idx_floor_empty", load().idx_floor_empty(blocks, _stream(torch.cuda.current_device())))
+
+
+def idx_floor_read(src, nbytes, sink, ticket=None, blocks=256, threads=256):
+    """Stream-read the first `nbytes` bytes of `src` (measurement floor); with a
+    zeroed one-word `ticket`, every workgroup then takes a ticket on it."""
+    dev = _dev(src, sink, ticket)
+    if nbytes > src.numel() * src.element_size() or sink.numel() < blocks:
+        raise ValueError("idx_floor_read: buffer too small")
+    _check("idx_floor_read", load().idx_floor_read(_ptr(src), nbytes, _ptr(sink), _ptr(ticket),
+                                                   blocks, threads, _stream(dev)))

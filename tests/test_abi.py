@@ -3,6 +3,7 @@ declares, and rejects bad arguments with the documented status before any HIP
 call. Every call here fails validation, so no kernel is ever launched (the
 pointers are never dereferenced)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -12,14 +13,14 @@ import pytest
 import block_scoring_top_amd as idx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "idx.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
 P = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
 
 
 def declared():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(idx_\w+)\s*\(", src)))
 
@@ -143,3 +144,18 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(idx, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         idx.load()
+
+
+def test_floor_launches_reject_bad_arguments(lib):
+    assert "idx_floor_empty" in declared() and "idx_floor_read" in declared()
+    assert lib.idx_floor_empty(0, None) == INVALID
+    assert lib.idx_floor_empty(65537, None) == INVALID
+    r = lib.idx_floor_read
+    assert r(None, 1024, P, None, 4, 256, None) == INVALID      # no source
+    assert r(P, 1024, None, None, 4, 256, None) == INVALID      # no sink
+    assert r(P, 0, P, None, 4, 256, None) == INVALID            # nothing to read
+    assert r(P, 1000, P, None, 4, 256, None) == INVALID         # not whole 16-byte words
+    assert r(P + 8, 1024, P, None, 4, 256, None) == INVALID     # misaligned source
+    assert r(P, 1024, P, None, 0, 256, None) == INVALID         # no workgroups
+    assert r(P, 1024, P, None, 4, 512, None) == INVALID         # unsupported block size
+    assert r(P, 1024, P, P + 2, 4, 256, None) == INVALID        # misaligned ticket
