@@ -107,6 +107,9 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted, stream));
 }
 
+// largest score-ordered K that 256-thread workgroups sort (four ids per thread)
+constexpr int kNarrowMaxSortedK = 1024;
+
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {
   (void)H; (void)K; (void)flags;
   if (B < 1 || N_pad < 1) return 0;
@@ -129,7 +132,9 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
   uint32_t* tickets = static_cast<uint32_t*>(ws);
   float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
-  const bool wide = B <= kWideMaxRequests;
+  // 1024-thread workgroups for a few requests, 256-thread ones for many; the
+  // score order of more than 1024 ids is sorted by 1024-thread workgroups only
+  const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
   const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
   return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad,

@@ -62,7 +62,9 @@ __device__ __forceinline__ uint32_t readlane<uint32_t>(uint32_t v, int l) {
 // lane's register inside the VALU, with no trip through LDS.
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
-constexpr int kDppRowShr1 = 0x111;    // row_shr:n = 0x110 + n, within 16-lane rows
+constexpr int kDppRowShl1 = 0x101;    // row_shl:n = 0x100 + n: lane l <- lane l + n of its row
+constexpr int kDppRowShr1 = 0x111;    // row_shr:n = 0x110 + n: lane l <- lane l - n of its row
+constexpr int kDppRowRor1 = 0x121;    // row_ror:n = 0x120 + n: rotation within the row
 constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i of its row
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i of its half row
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row -> the next row

@@ -44,12 +44,14 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__
                                                        int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ counts, int N,
                                                        int K) {
-  __shared__ SelectSmem<kTopkNT, kTopkSlots, SORTED> sm;
+  __shared__ SelectSmem<kTopkNT, kTopkSlots> sm;
+  extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<kTopkNT, kTopkSlots, SORTED, false, BLOCKED>(scores + (size_t)b * N, n, N, K, ids + (size_t)b * K,
-                                          counts ? counts + b : nullptr, sm);
+  select_row<kTopkNT, kTopkSlots, SORTED, false, BLOCKED>(
+      scores + (size_t)b * N, n, N, K, ids + (size_t)b * K, counts ? counts + b : nullptr, sm,
+      sort_lds);
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
@@ -60,8 +62,9 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, float* __restrict__ scores_out,
     int H, int N_pad, int page_size, int K, int chunk, int nchunk, uint32_t* tickets,
     float* stage, int stage_stride) {
-  __shared__ SelectSmem<NT, SLOTS, SORTED> sm;
+  __shared__ SelectSmem<NT, SLOTS> sm;
   __shared__ int s_last;
+  extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x - b * nchunk;
   // the summed query and the request length are loaded together (one round trip)
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   select_row<NT, SLOTS, SORTED, true, BLOCKED>(row, nv, row_cap, K, ids + (size_t)b * K,
-                                      counts ? counts + b : nullptr, sm,
+                                      counts ? counts + b : nullptr, sm, sort_lds,
                                       scores_out != nullptr ? nullptr : row);
 }
 
@@ -128,8 +131,8 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
   // fully coalesced); the blocked layout's strided loads cost more than its
   // cheaper emit saves.
   if (sorted)
-    hipLaunchKernelGGL((topk_kernel<true, false>), grid, block, 0, s, scores, n_valid, ids,
-                       counts, N, K);
+    hipLaunchKernelGGL((topk_kernel<true, false>), grid, block, sort_lds_bytes(K), s, scores,
+                       n_valid, ids, counts, N, K);
   else
     hipLaunchKernelGGL((topk_kernel<false, false>), grid, block, 0, s, scores, n_valid, ids,
                        counts, N, K);
@@ -150,7 +153,8 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
   const bool blocked = N_pad <= 8192;
   const bool short_rows = N_pad <= 2048;
 #define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_, BL)                                                 \
-  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL>), grid, dim3(NT_), 0, s, q, c, \
+  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL>), grid, dim3(NT_),           \
+                     SO ? sort_lds_bytes(K) : 0, s, q, c,                                      \
                      seq_len, ids, counts, scores_out, H, N_pad, page_size, K, chunk, nchunk,  \
                      tickets, stage, stage_stride)
 #define IDX_LAUNCH_FUSED_NT(BF, SO)                                                  \

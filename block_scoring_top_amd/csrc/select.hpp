@@ -1,27 +1,34 @@
-// Exact row top-K by 4-pass 8-bit radix select ("Iterate Topk": 8-bit radix
-// top-K; "Round 18 Track C", section 1 Target 1: four passes over uint order
-// keys, a 256-bin histogram scanned from the top bin down to find the bin that
-// holds the K-th key and how many keys of that bin are still needed, keys
+// Exact row top-K by radix select ("Iterate Topk": radix top-K over order keys;
+// "Round 18 Track C", section 1 Target 1: passes over unsigned order keys, each
+// a histogram of the next digit scanned from the top bin down to find the bin
+// that holds the K-th key and how many keys of that bin are still needed, keys
 // cached in registers for short rows). Ties are taken in ascending index order,
 // which the pages' bitwise id checks with adversarial ties require.
 //
-// One workgroup of NT threads selects one row. Keys live in registers in a
-// striped layout: slot i of thread t holds the 4 consecutive entries starting
-// at 4*(i*NT + t), so every load is a coalesced 16-byte vector load and, for a
-// fixed slot, the workgroup holds one contiguous index range. Rows longer than
-// one register tile (NT*SLOTS*4 entries) are streamed tile by tile each pass.
+// Digits here are 11, 11 and 10 bits (three passes instead of the pages' four
+// 8-bit ones: a 2048-bin histogram is 8 KiB of LDS, and every pass costs a few
+// barriers, which dominate at these row lengths). A pass stops the select
+// early when the chosen bin is taken whole, or when every key still in play is
+// the same value.
 //
-// Histogram: per-wave 256-bin sub-histograms in LDS. Before the LDS atomics a
-// wave peels off the group of lanes that share the first active lane's digit
-// and adds that group with one atomic; on degenerate rows (all equal, few
-// distinct values) this removes the same-address atomic serialisation.
+// One workgroup of NT threads selects one row. Keys live in registers, in one
+// of two layouts. Striped: slot i of thread t holds the 4 consecutive entries
+// starting at 4*(i*NT + t), so every load is a coalesced 16-byte vector load
+// and rows longer than one register tile (NT*SLOTS*4 entries) are streamed
+// tile by tile each pass. Blocked: thread t holds one run of consecutive
+// entries, which makes the emit a single scan (rows that fit one tile).
+//
+// Histogram: one 2048-bin histogram in LDS (two, alternating by pass, so one is
+// cleared while the other is read). Before the LDS atomics a wave peels off the
+// group of lanes that share the first active lane's digit and adds that group
+// with one atomic; on degenerate rows (all equal, few distinct values) this
+// removes the same-address atomic serialisation.
 //
 // Emit: a key is taken if its resolved digits exceed the threshold prefix, or
 // equal it and fewer than `need` equal keys precede it. Output positions come
-// from ballot/mbcnt counts inside a wave plus one workgroup scan over
-// (slot, wave) counts, so ids are written in ascending index order without any
-// atomics (deterministic). The sorted order (score desc, id asc) is then a rank
-// count over the selected (key, id) pairs in LDS.
+// from in-wave counts plus one workgroup scan, so ids are written in ascending
+// index order without atomics (deterministic). The score order (score desc,
+// id asc) is a bitonic sort of the selected (key, ~id) pairs as 64-bit words.
 #pragma once
 
 #include "common.hpp"
@@ -36,7 +43,7 @@ __device__ __forceinline__ int digit_shift(int p) {
 }
 __device__ __forceinline__ uint32_t digit_mask(int p) { return p == 2 ? 0x3FFu : 0x7FFu; }
 
-template <int NT, int SLOTS, bool SORTED>
+template <int NT, int SLOTS>
 struct SelectSmem {
   static constexpr int NW = NT / kWave;
   static constexpr int E = SLOTS * NW;  // emit-count entries per tile
@@ -47,8 +54,6 @@ struct SelectSmem {
   uint32_t sel_bin, sel_need, sel_tot, n_cand;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
-  alignas(16) uint32_t skey[SORTED ? kMaxSortedK + 4 : 1];
-  int32_t sid[SORTED ? kMaxSortedK : 1];
 };
 
 // Loads one register tile of keys. Every load of the tile is issued before any
@@ -224,48 +229,147 @@ __device__ __forceinline__ void wave0_scan2(uint32_t* a, uint32_t* b, uint32_t* 
   }
 }
 
-// Counts, for element i of keys[0..m) (LDS, zero-padded to a multiple of 4),
-//   gt = #{j : keys[j] > keys[i]}  and  tie = #{j < i : keys[j] == keys[i]}
-//   (or, with TIES_ALL, eq = #{j : keys[j] == keys[i]}).
-// Four adjacent lanes share one element, each counting a quarter of the groups
-// of 4 keys, and their counts are summed across the quad; every loop is uniform
-// across the wave. fn(i, key_i, gt, tie_or_eq) is called by the quad's first lane.
-template <int NT, bool TIES_ALL, typename Fn>
-__device__ __forceinline__ void quad_rank(const uint32_t* keys, int m, Fn fn) {
-  const int t = threadIdx.x;
-  const int part = t & 3;
-  const int ng = (m + 3) / 4;
-  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-  for (int i0 = 0; i0 < m; i0 += NT / 4) {
-    const int i = i0 + (t >> 2);
-    const uint32_t ki = i < m ? keys[i] : 0xFFFFFFFFu;
-    uint32_t gt = 0, tie = 0;
-    // groups part, part+4, ...: four groups are read before any is compared
-    for (int g0 = 0; g0 < ng; g0 += 16) {
-      uint4 v[4];
+// Bytes of dynamic LDS the score-ordered output needs for up to K ids: one
+// 64-bit word per id, K rounded up to a power of two (at least 4).
+__host__ __device__ inline int sort_lds_bytes(int K) {
+  int p = 4;
+  while (p < K) p <<= 1;
+  return p * 8;
+}
+
+// The value of lane (lane ^ M) for M a power of two below 64, without LDS:
+// DPP within a 16-lane row (quad permutes, row shifts, row rotation) and the
+// gfx950 row-swap permutes across rows.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (M == 1) {
+    return dpp_u32<kDppQuadXor1>(v);
+  } else if constexpr (M == 2) {
+    return dpp_u32<kDppQuadXor2>(v);
+  } else if constexpr (M == 4) {
+    const uint32_t up = dpp_u32<kDppRowShl1 + 3>(v);  // lane l + 4
+    const uint32_t dn = dpp_u32<kDppRowShr1 + 3>(v);  // lane l - 4
+    return (lane_id() & 4) ? dn : up;
+  } else if constexpr (M == 8) {
+    return dpp_u32<kDppRowRor1 + 7>(v);  // rotation by 8 within the row
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  return (uint64_t)lane_xor<M>((uint32_t)(v >> 32)) << 32 | lane_xor<M>((uint32_t)v);
+}
+
+// One compare-exchange stage of a descending bitonic sort over elements held E
+// per thread (element i = E*t + e in v[e]): partner i ^ J, and the pair is in
+// descending order when bit k of i is clear. J < E pairs registers of one
+// thread, E <= J < 64E lanes of one wave.
+template <int E, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[E], int t, int k) {
+  if constexpr (J < E) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int g = g0 + 4 * u + part;
-        v[u] = k4[g < ng ? g : 0];
+    for (int e = 0; e < E; ++e) {
+      if ((e & J) == 0) {
+        const bool desc = ((E * t + e) & k) == 0;
+        const uint64_t a = v[e], b = v[e | J];
+        const bool sw = desc ? a < b : a > b;
+        v[e] = sw ? b : a;
+        v[e | J] = sw ? a : b;
       }
+    }
+  } else {
+    constexpr int M = J / E;  // lane distance
+    const bool lower = (t & M) == 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int g = g0 + 4 * u + part;
-        if (g < ng) {
-          const uint32_t kv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    for (int e = 0; e < E; ++e) {
+      const uint64_t u = lane_xor64<M>(v[e]);
+      const bool keep_max = lower == (((E * t + e) & k) == 0);
+      v[e] = (keep_max == (u > v[e])) ? u : v[e];
+    }
+  }
+}
+
+// the in-wave tail of a merge of size k: stages J, J/2, ..., 1
+template <int E, int J>
+__device__ __forceinline__ void bitonic_merge_tail(uint64_t (&v)[E], int t, int k) {
+  bitonic_stage<E, J>(v, t, k);
+  if constexpr (J > 1) bitonic_merge_tail<E, J / 2>(v, t, k);
+}
+
+// Bitonic sort into descending order of P 64-bit words (P a power of two,
+// 64E <= P <= E * NT, or P < 64E with E == 1), E per thread: thread t < P / E
+// holds elements E*t .. E*t+E-1 in v[0..E); the other threads hold nothing
+// and skip the work, but take part in every barrier. Merges of up to 64E
+// elements stay inside one wave (registers and cross-lane moves, no LDS); the
+// stages of larger merges whose partners sit in another wave go through
+// `xbuf` (P words of LDS), two barriers each.
+template <int NT, int E>
+__device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int P, uint64_t* xbuf) {
+  const int t = threadIdx.x;
+  const bool live = E * t < P;
+  const bool wave_live = E * (t & ~(kWave - 1)) < P;  // uniform per wave
+  if (wave_live) {
+#define IDX_BITONIC_RUN(KK, JJ)                                   \
+  if constexpr (64 * E >= KK) {                                   \
+    if (P >= KK) bitonic_merge_tail<E, JJ>(v, t, KK);             \
+  }
+    IDX_BITONIC_RUN(2, 1)
+    IDX_BITONIC_RUN(4, 2)
+    IDX_BITONIC_RUN(8, 4)
+    IDX_BITONIC_RUN(16, 8)
+    IDX_BITONIC_RUN(32, 16)
+    IDX_BITONIC_RUN(64, 32)
+    IDX_BITONIC_RUN(128, 64)
+    IDX_BITONIC_RUN(256, 128)
+#undef IDX_BITONIC_RUN
+  }
+  for (int k = 128 * E; k <= P; k <<= 1) {
+    for (int j = k >> 1; j >= 64 * E; j >>= 1) {
+      __syncthreads();  // earlier readers of xbuf are done
+      if (live) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            gt += kv[c] > ki ? 1u : 0u;
-            tie += (kv[c] == ki && (TIES_ALL || 4 * g + c < i)) ? 1u : 0u;
-          }
+        for (int e = 0; e < E; ++e) xbuf[E * t + e] = v[e];
+      }
+      __syncthreads();
+      if (live) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = E * t + e;
+          const uint64_t u = xbuf[i ^ j];
+          const bool keep_max = ((i & j) == 0) == ((i & k) == 0);
+          v[e] = (keep_max == (u > v[e])) ? u : v[e];
         }
       }
     }
-    gt += dpp_u32<kDppQuadXor1>(gt);
-    gt += dpp_u32<kDppQuadXor2>(gt);
-    tie += dpp_u32<kDppQuadXor1>(tie);
-    tie += dpp_u32<kDppQuadXor2>(tie);
-    if (part == 0 && i < m) fn(i, ki, gt, tie);
+    if (wave_live) bitonic_merge_tail<E, 32 * E>(v, t, k);
+  }
+}
+
+// Sorts the m pairs in sortbuf[0..m) into descending order and writes the low
+// words, inverted, to ids_out[0..m): E = 1 up to NT pairs (one per thread),
+// else P / NT per thread.
+template <int NT, int E>
+__device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
+                                                int32_t* ids_out) {
+  const int t = threadIdx.x;
+  __syncthreads();  // every pair is in sortbuf
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * t + e;
+    v[e] = i < m ? sortbuf[i] : 0ull;
+  }
+  bitonic_desc<NT, E>(v, P, sortbuf);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * t + e;
+    if (i < m) ids_out[i] = (int32_t)~(uint32_t)v[e];
   }
 }
 
@@ -276,7 +380,8 @@ __device__ __forceinline__ void quad_rank(const uint32_t* keys, int m, Fn fn) {
 template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED>
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
                                                          int32_t* ids_out, int32_t* count_out,
-                                                         SelectSmem<NT, SLOTS, SORTED>& sm,
+                                                         SelectSmem<NT, SLOTS>& sm,
+                                                         uint64_t* sortbuf,
                                                          float* stage_zero = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
@@ -436,8 +541,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
           const int id = t * kpt4 + 4 * i + j;
           if constexpr (SORTED) {
-            sm.skey[pos] = keys[i][j];
-            sm.sid[pos] = id;
+            sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
           } else {
             ids_out[pos] = id;
           }
@@ -500,8 +604,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
           const int id = tbase + (i * NT + t) * 4 + j;
           if constexpr (SORTED) {
-            sm.skey[pos] = keys[i][j];
-            sm.sid[pos] = id;
+            sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
           } else {
             ids_out[pos] = id;
           }
@@ -518,13 +621,19 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   if (count_out != nullptr && t == 0) *count_out = (int32_t)m_out;
 
   if constexpr (SORTED) {
-    if (t < 4) sm.skey[m_out + t] = 0u;  // padding: below every key, never counted
-    __syncthreads();
-    // rank of pair i = number of pairs with a larger key, or an equal key and a
-    // smaller id (pairs are stored in ascending id order)
-    quad_rank<NT, false>(sm.skey, (int)m_out, [&](int i, uint32_t, uint32_t gt, uint32_t tie) {
-      ids_out[gt + tie] = sm.sid[i];
-    });
+    // (key << 32 | ~id) is unique per pair and orders by key, then by lower id;
+    // zero (below every key) pads the sort up to a power of two
+    int P = 2;
+    while (P < (int)m_out) P <<= 1;
+    if (P <= NT) {
+      sort_pairs_desc<NT, 1>(sortbuf, (int)m_out, P, ids_out);
+    } else if (P == 2 * NT) {
+      sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, ids_out);
+    } else {
+      // P == 4 * NT: callers give 256-thread workgroups at most 1024 ids to
+      // order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
+      sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, ids_out);
+    }
   }
   if (stage_zero != nullptr) {
     if (!cached) __syncthreads();  // streamed rows: every read of the row is done

@@ -120,6 +120,20 @@ def test_select_many_requests_medium_rows():
     full_select_check(x, 700, True)
 
 
+@pytest.mark.parametrize("K", [2, 64, 65, 1024, 1025, 2049, 4096])
+def test_select_sorted_sizes(K):
+    """Score order around the sort's size steps: in-thread, in-wave and across
+    waves, with 1024-thread workgroups (few requests) and 256-thread workgroups
+    (many requests; above 1024 ids the sort runs in LDS)."""
+    x = synth.make_indexer(3, 4, 128, 6000, [6000 * 16, 4100 * 16, 700 * 16], K, "bf16", 320 + K)
+    full_select_check(x, K, True)
+    rng = np.random.default_rng(340 + K)
+    seq = rng.integers(0, 5000 * 16, 40)
+    seq[:2] = [5000 * 16, 3000 * 16]
+    x = synth.make_indexer(40, 2, 128, 5000, seq, K, "bf16", 340 + K)
+    full_select_check(x, K, True)
+
+
 def test_select_many_requests_multi_tile():
     """More than 32 requests with rows longer than one 8192-key register tile."""
     x = synth.make_indexer(33, 2, 128, 9000, [9000 * 16] * 30 + [8193 * 16, 5, 8192 * 16],
@@ -240,7 +254,7 @@ def test_topk_adversarial_rows(sorted_out):
             rng.standard_normal(N).astype(np.float32)]
     s = np.stack(rows)
     nv = [N, N, N, N, 37, 0]
-    for K in (1, 100, 2048, 5000):
+    for K in (1, 100, 2048, 4096, 5000):
         if sorted_out and K > 4096:
             continue  # sorted output is limited to K <= 4096
         say(f"[topk] adversarial K={K} sorted={sorted_out}")
@@ -333,3 +347,25 @@ def test_workload_assign():
     rows = np.concatenate([np.arange(64), rng.choice(x.x.shape[0], 8192, replace=False),
                            np.arange(x.x.shape[0] - 64, x.x.shape[0])])
     assert check_assign(a, best, x.x, x.c, rows) == 0
+
+
+@pytest.mark.gpu
+def test_floor_launches_run_and_leave_the_ticket_at_zero():
+    import torch
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.full((512,), 7.0, dtype=torch.float32, device="cuda")
+    ticket = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx.idx_floor_empty(128)
+    for blocks, threads in ((1, 256), (37, 256), (512, 1024)):
+        sink.fill_(7.0)
+        idx.idx_floor_read(src, 4 << 20, sink, ticket, blocks, threads)
+        torch.cuda.synchronize()
+        assert int(ticket.item()) == 0
+        # every workgroup wrote its word (xor of its share of the arange)
+        w = sink[:blocks].view(torch.int32).cpu().numpy()
+        n16 = (4 << 20) // 16
+        per = -(-n16 // blocks)
+        a = np.arange(1 << 20, dtype=np.int64).reshape(-1, 4)
+        for g in range(blocks):
+            part = a[g * per:min((g + 1) * per, n16)]
+            assert int(w[g]) == int(np.bitwise_xor.reduce(part.ravel()))
