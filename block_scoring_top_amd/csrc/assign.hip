@@ -29,10 +29,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAsgNT = 256;          // 4 waves
 constexpr int kAsgPtsPerWave = 64;   // two 32-point column blocks
+constexpr int kCB = kAsgPtsPerWave / 32;  // 32-point column blocks per wave
 constexpr int kAsgPts = kAsgPtsPerWave * (kAsgNT / kWave);
 constexpr int kAsgTileC = 64;        // centroids per LDS tile: two 32-row blocks
 constexpr int kChunks = kHeadDim * 2 / 16;                // 16-byte chunks per bf16 row (16)
 constexpr int kTileLoads = kAsgTileC * kChunks / kAsgNT;  // 16-byte loads per thread per tile
+static_assert(kTileLoads * kAsgNT == kAsgTileC * kChunks, "whole loads per thread");
 
 // -|c_j|^2 / 2 in fp32, once per call (squares of bf16 values are exact in fp32),
 // padded with -inf up to a whole number of centroid tiles
@@ -65,8 +67,11 @@ __device__ __forceinline__ int swz(int r, int k) { return r * kChunks + (k ^ (r 
 // Load i of wave w fills the 64 consecutive 16-byte LDS slots p = 64 (4w + i) +
 // lane; slot p holds chunk (p & 15) ^ (row & 15) of tile row p >> 4, which is
 // the swizzled layout the MFMA operand reads expect. Rows past C repeat row C-1
-// (their bias is -inf, so they never win). Wave w < kAsgTileC/64 also brings 64
-// of the tile's biases from the -inf-padded norm buffer.
+// (their bias is -inf, so they never win). Each wave also brings 16 of the
+// tile's biases from the -inf-padded norm buffer, so every wave issues the same
+// kLoadsPerTile loads per tile.
+constexpr int kBiasPerWave = kAsgTileC / (kAsgNT / kWave);
+constexpr int kLoadsPerTile = kTileLoads + 1;
 __device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
                                                const float* __restrict__ cn, int C, int j0,
                                                uint4* tile, float* tn) {
@@ -81,8 +86,108 @@ __device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
     const int j = j0 + row < C ? j0 + row : C - 1;
     __builtin_amdgcn_global_load_lds(c + (size_t)j * kHeadDim + k * 8, tile + slot0, 16, 0, 0);
   }
-  if (w < kAsgTileC / kWave)
-    __builtin_amdgcn_global_load_lds(cn + j0 + w * kWave + lane, tn + w * kWave, 4, 0, 0);
+  if (lane < kBiasPerWave)
+    __builtin_amdgcn_global_load_lds(cn + j0 + w * kBiasPerWave + lane, tn + w * kBiasPerWave, 4,
+                                     0, 0);
+}
+
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+struct ArgmaxState {
+  float best[kCB];
+  int bidx[kCB];
+};
+
+// One centroid tile: A fragments and biases from LDS tile `cur`, then (once
+// they are in registers) the direct-to-LDS load of tile `tile + 2` into `nxt`,
+// the products, the running argmax, and the wait for tile `tile + 1`.
+__device__ __forceinline__ void assign_tile(const uint16_t* __restrict__ c,
+                                            const float* __restrict__ cn, int C, int tile,
+                                            int ntiles, const uint4* cur, const float4* curn,
+                                            uint4* nxt, float* nxtn, const uint4 (&xb)[kCB][8],
+                                            ArgmaxState& st) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int j0 = tile * kAsgTileC;
+  bf16x8 a[8][2];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    a[ks][0] = as_bf16x8(cur[swz(col, 2 * ks + half)]);
+    a[ks][1] = as_bf16x8(cur[swz(32 + col, 2 * ks + half)]);
+  }
+  float4 bias[2][4];  // rows 8g + 4*half + 0..3 of 32-row block rb
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bias[rb][g] = curn[rb * 8 + 2 * g + half];
+  const bool refill = tile + 2 < ntiles;
+  if (refill) load_ctile_lds(c, cn, C, j0 + 2 * kAsgTileC, nxt, nxtn);
+
+  // independent accumulator chains: 2 centroid blocks x kCB point blocks
+  f32x16 acc[2][kCB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[rb][cb][4 * g + 0] = bias[rb][g].x;
+        acc[rb][cb][4 * g + 1] = bias[rb][g].y;
+        acc[rb][cb][4 * g + 2] = bias[rb][g].z;
+        acc[rb][cb][4 * g + 3] = bias[rb][g].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const bf16x8 b = as_bf16x8(xb[cb][ks]);
+      acc[0][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][0], b, acc[0][cb], 0, 0, 0);
+      acc[1][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][1], b, acc[1][cb], 0, 0, 0);
+    }
+  }
+  // Running argmax. The 16 values of a lane are reduced with 3-input maxes;
+  // only when some lane of the wave finds a strictly larger value is the index
+  // of its first (lowest-index) occurrence searched. For a fixed lane the
+  // centroid index increases with (tile, rb, r), so strict comparisons keep
+  // the lowest index among equal values.
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const f32x16& v = acc[rb][cb];
+      float m = v[0];
+#pragma unroll
+      for (int r = 1; r < 15; r += 2)  // a chain of 3-input maxes
+        m = __builtin_fmaxf(__builtin_fmaxf(m, v[r]), v[r + 1]);
+      m = __builtin_fmaxf(m, v[15]);
+      const bool better = m > st.best[cb];
+      if (__builtin_amdgcn_ballot_w64(better) != 0) {
+        int rr = 15;
+#pragma unroll
+        for (int r = 14; r >= 0; --r) rr = (v[r] == m) ? r : rr;
+        if (better) {
+          st.best[cb] = m;
+          st.bidx[cb] = j0 + rb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
+        }
+      }
+    }
+  }
+  // Tile `tile + 1` has landed once at most the loads just issued for tile
+  // `tile + 2` are outstanding in this wave, and in every wave after the
+  // barrier; the barrier also frees `cur` for the refill issued next step.
+  // (A plain barrier: the fence of __syncthreads would wait for every load.)
+  if (refill) wait_vmcnt<kLoadsPerTile>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
 }
 
 __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __restrict__ x,
@@ -91,8 +196,10 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
                                                            int32_t* __restrict__ assign,
                                                            float* __restrict__ best_out,
                                                            int64_t N, int C) {
-  __shared__ uint4 ctile[2][kAsgTileC * kChunks];  // 2 x 16 KiB
-  __shared__ float4 ctn4[2][kAsgTileC / 4];
+  // three LDS tiles of 64 centroids (16 KiB each) and their biases, as
+  // separate objects: tile t+2 streams in while tile t is multiplied
+  __shared__ uint4 ct0[kAsgTileC * kChunks], ct1[kAsgTileC * kChunks], ct2[kAsgTileC * kChunks];
+  __shared__ float4 cn0[kAsgTileC / 4], cn1[kAsgTileC / 4], cn2[kAsgTileC / 4];
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
@@ -101,9 +208,9 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
   const int64_t p0 = (int64_t)blockIdx.x * kAsgPts + w * kAsgPtsPerWave;
 
   // B operand: this lane's point rows, all 128 dims, as 8 k-steps of 8 bf16
-  uint4 xb[2][8];
+  uint4 xb[kCB][8];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     int64_t p = p0 + cb * 32 + col;
     p = p < N ? p : N - 1;  // clamp: a valid duplicate row, never stored
     const uint4* xr = reinterpret_cast<const uint4*>(x + p * kHeadDim);
@@ -111,80 +218,36 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
     for (int ks = 0; ks < 8; ++ks) xb[cb][ks] = xr[2 * ks + half];
   }
 
-  float best[2] = {-__builtin_inff(), -__builtin_inff()};
-  int bidx[2] = {0, 0};
-
-  const int ntiles = (C + kAsgTileC - 1) / kAsgTileC;
-  load_ctile_lds(c, cn, C, 0, ctile[0], reinterpret_cast<float*>(ctn4[0]));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const int j0 = tile * kAsgTileC;
-    // the next tile streams into the idle buffer while this one is multiplied
-    if (tile + 1 < ntiles)
-      load_ctile_lds(c, cn, C, j0 + kAsgTileC, ctile[buf ^ 1],
-                     reinterpret_cast<float*>(ctn4[buf ^ 1]));
-
-    // four independent accumulator chains (2 centroid blocks x 2 point blocks)
-    // keep the matrix pipeline busy; A fragments are read one k-step ahead of use
-    f32x16 acc[2][2];
+  ArgmaxState st;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {  // rows 8g + 4*half + 0..3 of a 32-row block
-        const float4 bias = ctn4[buf][rb * 8 + 2 * g + half];
-        acc[rb][0][4 * g + 0] = acc[rb][1][4 * g + 0] = bias.x;
-        acc[rb][0][4 * g + 1] = acc[rb][1][4 * g + 1] = bias.y;
-        acc[rb][0][4 * g + 2] = acc[rb][1][4 * g + 2] = bias.z;
-        acc[rb][0][4 * g + 3] = acc[rb][1][4 * g + 3] = bias.w;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = as_bf16x8(ctile[buf][swz(col, 2 * ks + half)]);
-      const bf16x8 a1 = as_bf16x8(ctile[buf][swz(32 + col, 2 * ks + half)]);
-      const bf16x8 b0 = as_bf16x8(xb[0][ks]), b1 = as_bf16x8(xb[1][ks]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-    }
-    // Running argmax. The 16 values of a lane are reduced with 3-input maxes;
-    // only when some lane of the wave finds a strictly larger value is the index
-    // of its first (lowest-index) occurrence searched. For a fixed lane the
-    // centroid index increases with (tile, rb, r), so strict comparisons keep
-    // the lowest index among equal values.
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const f32x16& v = acc[rb][cb];
-        float m = v[0];
-#pragma unroll
-        for (int r = 1; r < 15; r += 2)  // a chain of 3-input maxes
-          m = __builtin_fmaxf(__builtin_fmaxf(m, v[r]), v[r + 1]);
-        m = __builtin_fmaxf(m, v[15]);
-        const bool better = m > best[cb];
-        if (__builtin_amdgcn_ballot_w64(better) != 0) {
-          int rr = 15;
-#pragma unroll
-          for (int r = 14; r >= 0; --r) rr = (v[r] == m) ? r : rr;
-          if (better) {
-            best[cb] = m;
-            bidx[cb] = j0 + rb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-    __syncthreads();                 // ... and every wave's; this buffer is free again
+  for (int cb = 0; cb < kCB; ++cb) {
+    st.best[cb] = -__builtin_inff();
+    st.bidx[cb] = 0;
   }
+  const int ntiles = (C + kAsgTileC - 1) / kAsgTileC;
+  load_ctile_lds(c, cn, C, 0, ct0, reinterpret_cast<float*>(cn0));
+  if (ntiles > 1) {
+    load_ctile_lds(c, cn, C, kAsgTileC, ct1, reinterpret_cast<float*>(cn1));
+    wait_vmcnt<kLoadsPerTile>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+
+  // unrolled by three so that every LDS access names its buffer at compile time
+  for (int tile = 0; tile < ntiles; tile += 3) {
+    assign_tile(c, cn, C, tile, ntiles, ct0, cn0, ct2, reinterpret_cast<float*>(cn2), xb, st);
+    if (tile + 1 >= ntiles) break;
+    assign_tile(c, cn, C, tile + 1, ntiles, ct1, cn1, ct0, reinterpret_cast<float*>(cn0), xb, st);
+    if (tile + 2 >= ntiles) break;
+    assign_tile(c, cn, C, tile + 2, ntiles, ct2, cn2, ct1, reinterpret_cast<float*>(cn1), xb, st);
+  }
+  float* best = st.best;
+  int* bidx = st.bidx;
 
   // merge the two lanes that share a point (l and l^32)
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const float ov = __shfl_xor(best[cb], 32, kWave);
     const int oi = __shfl_xor(bidx[cb], 32, kWave);
     if (ov > best[cb] || (ov == best[cb] && oi < bidx[cb])) {
