@@ -27,8 +27,8 @@ Prints one JSON line:
                         (alone, and followed by one arrival counter) on this GPU
 
 Other modes:
-  --workload N         1..5 (1: tiny fp32, 2: default, 3: top-K stress,
-                       4: large GQA batch, 5: k-means assignment)
+  --workload N         1..6 (1: tiny fp32, 2: default, 3: top-K stress,
+                       4: large GQA batch, 5: k-means assignment, 6: paged pool)
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
   --parse-pmc DIR      turn rocprofv3 --pmc output into a traffic summary
 """
@@ -53,7 +53,7 @@ ROTATE_BYTES = 512 << 20
 CALIB_BYTES = 1 << 30
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
-          4: "select_fused_kernel", 5: "assign_kernel"}
+          4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
            ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "api.cpp")]
 
@@ -131,6 +131,61 @@ class Indexer:
             times.append(time.perf_counter() - t0)
         med = statistics.median(times)
         return self.units / med, f"the whole batch ({self.units} valid blocks), {len(times)} " \
+                                 f"calls, median {med * 1e3:.1f} ms per call"
+
+
+class Paged:
+    def __init__(self, x, torch, idx, copies):
+        self.x, self.torch, self.idx = x, torch, idx
+        q, c = to_dev(x.q), to_dev(x.c_pool)
+        ip, ix = to_dev(x.indptr), to_dev(x.indices)
+        self.inputs = [(q, c, ip, ix)] + [(q.clone(), c.clone(), ip.clone(), ix.clone())
+                                          for _ in range(copies - 1)]
+        dev = q.device
+        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(x.B, dtype=torch.int32, device=dev)
+        nbytes = idx.idx_workspace_bytes(x.B, x.max_pages, x.H, x.K, 0)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        import numpy as np
+        n = np.minimum(np.diff(x.indptr.astype(np.int64)), x.max_pages)
+        self.nv = [int(v) for v in n]
+        self.units = int(n.sum())                      # page slots scored
+        elem = 2 if x.dtype == "bf16" else 4
+        unique_rows = int(np.unique(x.indices).size)   # pool rows the lists name
+        # pool rows named (each read from HBM at least once) + the page lists +
+        # query heads + ids written
+        self.alg_bytes = (unique_rows * 128 * elem + 4 * x.indices.size + 4 * (x.B + 1)
+                          + x.q.size * elem + 4 * x.B * x.K)
+        self.alg_flops = 2 * self.units * 128
+
+    def step(self, i, sorted=None):
+        q, c, ip, ix = self.inputs[i % len(self.inputs)]
+        self.idx.idx_select_paged(q, c, ip, ix, self.x.K, self.x.max_pages,
+                                  sorted=self.x.sorted if sorted is None else sorted,
+                                  ids=self.ids, counts=self.counts, ws=self.ws)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][1]
+
+    def describe(self):
+        x = self.x
+        return {"workload": x.name, "call": "idx_select_paged", "B": x.B, "H": x.H, "D": 128,
+                "pool_rows": int(x.c_pool.shape[0]), "max_pages": x.max_pages,
+                "page_slots": self.units, "K": x.K, "sorted": x.sorted, "inputs": x.dtype,
+                "accumulate": "f32", "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import oracle
+        x = self.x
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            S, _, n = oracle.score_paged(x.q, x.c_pool, x.indptr, x.indices, x.max_pages, x.dtype)
+            oracle.select(S, n, x.K, x.sorted)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        return self.units / med, f"the whole batch ({self.units} page slots), {len(times)} " \
                                  f"calls, median {med * 1e3:.1f} ms per call"
 
 
@@ -226,6 +281,8 @@ def make(w, torch, idx, copies):
         return Indexer(x, torch, idx, copies)
     if w == 3:
         return Topk(x, torch, idx, copies)
+    if w == 6:
+        return Paged(x, torch, idx, copies)
     return Assign(x, torch, idx, copies)
 
 
@@ -234,6 +291,8 @@ def input_bytes(w, x):
         return x.q.nbytes + x.c.nbytes
     if w == 3:
         return x.scores.nbytes
+    if w == 6:
+        return x.q.nbytes + x.c_pool.nbytes + x.indptr.nbytes + x.indices.nbytes
     return x.x.nbytes + x.c.nbytes
 
 
@@ -420,7 +479,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -531,7 +590,7 @@ def main():
         log("[bench] cold calls, host end-to-end, floors")
         extras["cold_us_per_call"] = stats_us(cold_times(torch, wl, 32))
         extras["host_e2e_us_per_call"] = stats_us(host_e2e_times(torch, wl, 32))
-        if a.workload in (2, 3, 4):  # headline unsorted; the score-ordered output beside it
+        if a.workload in (2, 3, 4, 6):  # headline unsorted; the score-ordered output beside it
             extras["sorted_us_per_call"] = min(graph_time(
                 torch, lambda i: wl.step(i, sorted=True), min(a.steps, 1000), 3)) * 1e3
         extras["floor"] = floors(torch, idx, wl, min(a.steps, 200))
@@ -550,7 +609,7 @@ def main():
     out = {
         "metric": METRIC,
         "value": wl.units * per_s,
-        "unit": {5: "points/s"}.get(a.workload, "entries/s" if a.workload == 3 else "blocks/s"),
+        "unit": {5: "points/s", 3: "entries/s", 6: "page slots/s"}.get(a.workload, "blocks/s"),
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
         "launch": launch_desc,

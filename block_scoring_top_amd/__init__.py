@@ -13,7 +13,7 @@ import threading
 
 import torch
 
-__all__ = ["idx_score", "idx_topk", "idx_select", "idx_assign", "idx_workspace_bytes",
+__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
            "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
 
@@ -32,6 +32,9 @@ _SIGS = {
     "idx_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
     "idx_select": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _u32, _vp, _c_size, _vp]),
+    "idx_select_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                  _c_int, ctypes.c_int64, _c_int, _c_int, _c_int, _u32, _vp,
+                                  _c_size, _vp]),
     "idx_assign_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "idx_assign": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int64, _c_int, _c_int, _c_int, _vp,
                             _c_size, _vp]),
@@ -182,6 +185,37 @@ def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False
     _check("idx_select", lib.idx_select(_ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts),
                                         _ptr(scores_out), B, H, D, N_pad, page_size, K,
                                         _dtype_code(q), flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return ids, counts, scores_out
+
+
+def idx_select_paged(q, c_pool, kv_indptr, kv_indices, K, max_pages, sorted=False,
+                     return_scores=False, ids=None, counts=None, scores_out=None, ws=None,
+                     chunk_log2=0):
+    """Fused score + top-K over a paged centroid pool: request b's slots are
+    kv_indices[kv_indptr[b]:kv_indptr[b+1]] (at most max_pages of them).
+    Returns (ids, counts, scores_out or None); ids are slot positions."""
+    lib = load()
+    dev = _dev(q, c_pool, kv_indptr, kv_indices, ids, counts, scores_out, ws)
+    if kv_indptr.dtype != torch.int32 or kv_indices.dtype != torch.int32:
+        raise TypeError("kv_indptr and kv_indices must be int32")
+    B, H, D = q.shape
+    if kv_indptr.numel() != B + 1:
+        raise ValueError("kv_indptr must hold B + 1 entries")
+    n_rows = c_pool.shape[0]
+    if ids is None:
+        ids = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    if return_scores and scores_out is None:
+        scores_out = torch.empty(B, max_pages, dtype=torch.float32, device=dev)
+    flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+    nbytes = lib.idx_workspace_bytes(B, max_pages, H, K, flags)
+    if ws is None:
+        ws = _workspace(dev, nbytes, "select")
+    _check("idx_select_paged", lib.idx_select_paged(
+        _ptr(q), _ptr(c_pool), _ptr(kv_indptr), _ptr(kv_indices), _ptr(ids), _ptr(counts),
+        _ptr(scores_out), B, H, D, n_rows, kv_indices.numel(), max_pages, K, _dtype_code(q),
+        flags, _ptr(ws), ws.numel(), _stream(dev)))
     return ids, counts, scores_out
 
 

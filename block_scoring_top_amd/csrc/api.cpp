@@ -139,7 +139,42 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
   return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad,
                                         page_size, K, dt == IDX_BF16, sorted, chunk, wide,
-                                        tickets, stage, stage_stride(N_pad), stream));
+                                        tickets, stage, stage_stride(N_pad), nullptr, nullptr, 0,
+                                        0, stream));
+}
+
+int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, int32_t* ids, int32_t* counts, float* scores_out,
+                     int B, int H, int D, int n_rows, int64_t n_indices, int max_pages, int K,
+                     idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (q == nullptr || c_pool == nullptr || kv_indptr == nullptr || ids == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (kv_indices == nullptr && n_indices > 0) return IDX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(c_pool, 16) || !aligned(kv_indptr, 4) ||
+      !aligned(kv_indices, 4) || !aligned(ids, 4) || !aligned(counts, 4) ||
+      !aligned(scores_out, 4))
+    return IDX_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || D < 1 || n_rows < 1 || n_indices < 0 || max_pages < 1 || K < 1)
+    return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if ((int64_t)B * max_pages > kMaxRows || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
+  if (H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
+  int st;
+  if ((st = check_chunk_flag(flags)) != IDX_OK) return st;
+  if (B > kMaxRequests) return IDX_ERR_UNSUPPORTED;
+  const bool sorted = (flags & IDX_SORTED) != 0;
+  if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
+  const size_t need = idx_workspace_bytes(B, max_pages, H, K, flags);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
+  uint32_t* tickets = static_cast<uint32_t*>(ws);
+  float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
+  const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
+  const int chunk = wide ? chunk_rows(B, max_pages, flags, kWideChunkMin, kWideTarget)
+                         : chunk_rows(B, max_pages, flags, kScoreChunkMin, kScoreTarget);
+  return hip_status(idxk::launch_select(q, c_pool, nullptr, ids, counts, scores_out, B, H,
+                                        max_pages, 1, K, dt == IDX_BF16, sorted, chunk, wide,
+                                        tickets, stage, stage_stride(max_pages), kv_indptr,
+                                        kv_indices, n_indices, n_rows, stream));
 }
 
 // -|c|^2/2 per centroid, padded with -inf to a multiple of 128 (a whole number of

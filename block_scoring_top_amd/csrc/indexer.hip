@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
   if (r1 > r0) {
     float qs[8];
     load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
-    score_rows<BF16, kScoreNT>(c, (size_t)b * N_pad, qs, r0, r1, dst);
+    score_rows<BF16, kScoreNT>(c, DenseRows{(size_t)b * N_pad}, qs, r0, r1, dst);
   }
   fill_neg_inf(dst, max(r0, nv), r_end);
 }
@@ -56,12 +56,16 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
 // NT threads per workgroup, select tile NT*SLOTS*4 keys.
-template <bool BF16, bool SORTED, int NT, int SLOTS, bool BLOCKED>
+// PAGED: request b's score slots are its page list indices[indptr[b] ..
+// indptr[b+1]) (at most N_pad of them) into a shared pool of n_rows centroids;
+// otherwise its N_pad rows of c, the first n_valid(seq_len[b]) of them scored.
+template <bool BF16, bool SORTED, int NT, int SLOTS, bool BLOCKED, bool PAGED>
 __global__ __launch_bounds__(NT) void select_fused_kernel(
     const void* __restrict__ q, const void* __restrict__ c, const int32_t* __restrict__ seq_len,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, float* __restrict__ scores_out,
     int H, int N_pad, int page_size, int K, int chunk, int nchunk, uint32_t* tickets,
-    float* stage, int stage_stride) {
+    float* stage, int stage_stride, const int32_t* __restrict__ indptr,
+    const int32_t* __restrict__ indices, int64_t n_indices, int n_rows) {
   __shared__ SelectSmem<NT, SLOTS> sm;
   __shared__ int s_last;
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
@@ -70,7 +74,16 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   // the summed query and the request length are loaded together (one round trip)
   float qs[8];
   load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
-  const int nv = n_valid_blocks(seq_len[b], page_size, N_pad);
+  int nv;
+  int64_t pbase = 0, avail = 0;
+  if constexpr (PAGED) {
+    const int lo = indptr[b], hi = indptr[b + 1];
+    nv = min(max(hi - lo, 0), N_pad);
+    pbase = lo;
+    avail = (lo >= 0 && (int64_t)lo < n_indices) ? n_indices - lo : 0;
+  } else {
+    nv = n_valid_blocks(seq_len[b], page_size, N_pad);
+  }
   const int n_part = max(1, (nv + chunk - 1) / chunk);
   const int r0 = ch * chunk;
   const int r_end = min(r0 + chunk, N_pad);
@@ -82,7 +95,14 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
                                      : stage + (size_t)b * stage_stride;
   const int row_cap = scores_out != nullptr ? N_pad : stage_stride;
   const int r1 = min(r_end, nv);
-  if (r1 > r0) score_rows<BF16, NT, true, (NT >= 1024 ? 2 : 4)>(c, (size_t)b * N_pad, qs, r0, r1, row);
+  if (r1 > r0) {
+    constexpr int U = NT >= 1024 ? 2 : 4;
+    if constexpr (PAGED)
+      score_rows<BF16, NT, true, U>(c, PagedRows{indices + (avail > 0 ? pbase : 0), avail, n_rows},
+                                    qs, r0, r1, row);
+    else
+      score_rows<BF16, NT, true, U>(c, DenseRows{(size_t)b * N_pad}, qs, r0, r1, row);
+  }
   if (scores_out != nullptr) fill_neg_inf(row, max(r0, nv), r_end);
 
   // Hand-off without cache-wide fences: the scores above were written with
@@ -142,7 +162,8 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
 int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
                   int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
                   int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
-                  float* stage, int stage_stride, void* stream) {
+                  float* stage, int stage_stride, const int32_t* indptr, const int32_t* indices,
+                  int64_t n_indices, int n_rows, void* stream) {
   const int nchunk = (N_pad + chunk - 1) / chunk;
   const dim3 grid((unsigned)B * nchunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -152,11 +173,20 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
   // 256-thread workgroups use 2 slots, 256*2*4 = 2048, when that is enough)
   const bool blocked = N_pad <= 8192;
   const bool short_rows = N_pad <= 2048;
-#define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_, BL)                                                 \
-  hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL>), grid, dim3(NT_),           \
-                     SO ? sort_lds_bytes(K) : 0, s, q, c,                                      \
-                     seq_len, ids, counts, scores_out, H, N_pad, page_size, K, chunk, nchunk,  \
-                     tickets, stage, stage_stride)
+  const bool paged = indptr != nullptr;
+#define IDX_LAUNCH_FUSED(BF, SO, NT_, SL_, BL)                                                  \
+  do {                                                                                         \
+    if (paged)                                                                                 \
+      hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL, true>), grid, dim3(NT_),   \
+                         SO ? sort_lds_bytes(K) : 0, s, q, c, seq_len, ids, counts,            \
+                         scores_out, H, N_pad, page_size, K, chunk, nchunk, tickets, stage,    \
+                         stage_stride, indptr, indices, n_indices, n_rows);                    \
+    else                                                                                       \
+      hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL, false>), grid, dim3(NT_),  \
+                         SO ? sort_lds_bytes(K) : 0, s, q, c, seq_len, ids, counts,            \
+                         scores_out, H, N_pad, page_size, K, chunk, nchunk, tickets, stage,    \
+                         stage_stride, indptr, indices, n_indices, n_rows);                    \
+  } while (0)
 #define IDX_LAUNCH_FUSED_NT(BF, SO)                                                  \
   if (wide) {                                                                        \
     if (blocked) IDX_LAUNCH_FUSED(BF, SO, 1024, 2, true);                            \

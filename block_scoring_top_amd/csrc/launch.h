@@ -14,10 +14,15 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
                 int B, int N, int K, bool sorted, void* stream);
 
+// indptr == nullptr: dense tables (c is [B, N_pad, 128], seq_len gives the
+// valid rows). Otherwise paged: c is a pool of n_rows centroids, request b's
+// slots are indices[indptr[b] .. indptr[b+1]) (n_indices entries exist), N_pad
+// is the longest page list, and seq_len / page_size are unused.
 int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
                   int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
                   int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
-                  float* stage, int stage_stride, void* stream);
+                  float* stage, int stage_stride, const int32_t* indptr, const int32_t* indices,
+                  int64_t n_indices, int n_rows, void* stream);
 
 int launch_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C,
                   float* cnorm, void* stream);

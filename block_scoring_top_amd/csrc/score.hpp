@@ -64,14 +64,34 @@ __device__ __forceinline__ void load_qsum(const void* q, int b, int H, int l16, 
   }
 }
 
-// Scores rows [r0, r1) of request b into dst[r] (dst = that request's score row).
+// Where score row r of a request reads its centroid. Dense tables: row
+// row_base + r. Paged tables: the request's page list holds the row, and a
+// slot whose entry lies outside [0, n_rows) (or past the list) is not a
+// candidate: it scores -inf and its centroid is never read.
+struct DenseRows {
+  size_t row_base;
+  __device__ __forceinline__ int64_t operator()(int r) const { return (int64_t)(row_base + r); }
+};
+struct PagedRows {
+  const int32_t* indices;  // the request's page list starts at indices[0]
+  int64_t avail;           // entries of the list that exist in memory
+  int n_rows;              // rows of the centroid pool
+  __device__ __forceinline__ int64_t operator()(int r) const {
+    if (r >= avail) return -1;
+    const int j = indices[r];
+    return (unsigned)j < (unsigned)n_rows ? (int64_t)j : -1;
+  }
+};
+
+// Scores rows [r0, r1) of one request into dst[r] (dst = that request's score row).
 // Rows are spread over the workgroup: wave w, lane group g = lane/16 takes rows
 // r0 + 16*NWAVES*... in steps; U row-steps are loaded before any is reduced so
-// that several loads per lane are in flight.
+// that several loads per lane are in flight (for paged tables the U page
+// entries are read first, then the U rows).
 // With COHERENT the scores are written with agent-scope stores, which are
 // visible to every XCD once complete (see the hand-off in the fused kernel).
-template <bool BF16, int NT, bool COHERENT = false, int U = 4>
-__device__ __forceinline__ void score_rows(const void* c, size_t row_base, const float (&qs)[8],
+template <bool BF16, int NT, bool COHERENT = false, int U = 4, typename RowOf>
+__device__ __forceinline__ void score_rows(const void* c, const RowOf& row_of, const float (&qs)[8],
                                            int r0, int r1, float* dst) {
   constexpr int NW = NT / kWave;
   constexpr int ROWS_PER_STEP = NW * 4;
@@ -81,13 +101,16 @@ __device__ __forceinline__ void score_rows(const void* c, size_t row_base, const
   const int my = (t >> 6) * 4 + (lane >> 4);  // row offset inside one step
   if (r1 <= r0) return;
   for (int base = r0; base < r1; base += ROWS_PER_STEP * U) {
-    RowLoad<BF16> ld[U];
+    int64_t j[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int r = base + u * ROWS_PER_STEP + my;
       r = r < r1 ? r : r1 - 1;  // clamp: a duplicate in-range read, result discarded
-      ld[u].load(c, row_base + (size_t)r, l16);
+      j[u] = row_of(r);
     }
+    RowLoad<BF16> ld[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ld[u].load(c, (size_t)(j[u] < 0 ? 0 : j[u]), l16);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float x[8];
@@ -96,6 +119,7 @@ __device__ __forceinline__ void score_rows(const void* c, size_t row_base, const
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc = fmaf(qs[k], x[k], acc);
       acc = sum16(acc);
+      if (j[u] < 0) acc = -__builtin_inff();
       const int r = base + u * ROWS_PER_STEP + my;
       if (l16 == 0 && r < r1) {
         if constexpr (COHERENT) {

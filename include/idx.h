@@ -138,6 +138,33 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
                size_t ws_bytes, void* stream);
 
 /*
+ * idx_select_paged -- idx_select over a paged centroid pool ([CS] submission
+ * contract and benchmark protocol: the scorer reads each request's pages
+ * through its context (page lists cut into work tiles) from a pool of block
+ * centroids, n_blocks = 16384 in the benchmark sweep).
+ *   c_pool     [n_rows, D] centroids (16-byte aligned), shared by all requests
+ *   kv_indptr  [B+1] int32 device array; request b's score slots are
+ *              i = 0 .. kv_indptr[b+1] - kv_indptr[b] - 1, slot i reading the
+ *              pool row kv_indices[kv_indptr[b] + i]
+ *   kv_indices [n_indices] int32 device array of pool rows
+ *   s[b,i] = sum_h q[b,h,:] . c_pool[kv_indices[kv_indptr[b] + i], :]
+ * A request's slot count is clamped to [0, max_pages]. A slot whose list entry
+ * does not exist (position outside [0, n_indices)) or names a row outside
+ * [0, n_rows) is not a candidate: it scores -inf and nothing is read for it.
+ * ids, counts and the selection rule are those of idx_select, with slot
+ * positions i as the ids (the caller maps them to pool rows through its lists).
+ *   scores_out [B, max_pages] float32 output or NULL (-inf past a request's slots)
+ * Workspace: idx_workspace_bytes(B, max_pages, H, K, flags), with the same
+ * zero-fill rule as idx_select.
+ * B >= 1, n_rows >= 1, n_indices >= 0, max_pages >= 1, K >= 1; other limits as
+ * idx_select.
+ */
+int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, int32_t* ids, int32_t* counts, float* scores_out,
+                     int B, int H, int D, int n_rows, int64_t n_indices, int max_pages, int K,
+                     idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * idx_assign -- nearest-centroid k-means assignment ([KM] Summary): the select
  * step with K = 1 over a dense score matrix.
  *   assign[i] = argmax_j ( 2 * x[i,:].c[j,:] - |c[j,:]|^2 ), ties to the lower j,

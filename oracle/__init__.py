@@ -14,6 +14,10 @@ sort, an argmax) as its only building blocks:
           centroids, feeding the downstream top-K; "Round 18 Track C", section
           1 Target 2: the per-block score sums the query heads' dot products
           with the block key over 128 dims.)
+  score_paged  the same score for pages addressed through per-request page
+          lists into a shared pool of centroids ("Iterate Centroids Score",
+          submission contract and benchmark protocol: the scorer reads a
+          request's pages through its context, from a pool of 16384 blocks).
   select  the K highest-scoring valid blocks of each row, ties to the lower
           block id ("Iterate Topk": top-K indices from per-segment scores;
           "Round 18 Track C", section 2: ids compared exactly, with
@@ -41,7 +45,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_decode", "to_f64", "n_valid", "score", "select", "select_row",
+__all__ = ["bf16_decode", "to_f64", "n_valid", "score", "score_paged", "select", "select_row",
            "assign", "assign_scores"]
 
 
@@ -97,6 +101,42 @@ def score(q, c, seq_len, page_size: int, dtype: str):
         S[b, :m] = per_head.sum(axis=1)            # then sum over heads
         A[b, :m] = (np.abs(cb) @ np.abs(qf[b]).T).sum(axis=1)
     return S, A
+
+
+def score_paged(q, c_pool, indptr, indices, max_pages: int, dtype: str):
+    """Scores of paged requests in float64, their error scale and slot counts.
+
+    Request b owns slots i = 0 .. n_b - 1, n_b = min(max(indptr[b+1] - indptr[b],
+    0), max_pages); slot i is pool row indices[indptr[b] + i]. A slot whose list
+    position lies outside the list, or whose row lies outside the pool, is not
+    a candidate (reading: such an entry names no page; it scores -inf).
+    Returns (S, A, n_slots): S, A float64 [B, max_pages] as in score(), -inf / 0
+    past a request's slots; n_slots int64 [B].
+    ("Iterate Centroids Score", submission contract and benchmark protocol.)
+    """
+    qf = to_f64(q, dtype)
+    B = qf.shape[0]
+    pool = to_f64(c_pool, dtype)
+    indptr = np.asarray(indptr, dtype=np.int64)
+    indices = np.asarray(indices, dtype=np.int64)
+    S = np.full((B, max_pages), -np.inf)
+    A = np.zeros((B, max_pages))
+    n_slots = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        lo = int(indptr[b])
+        n = min(max(int(indptr[b + 1]) - lo, 0), max_pages)
+        n_slots[b] = n
+        pos = lo + np.arange(n)
+        ok = (pos >= 0) & (pos < len(indices))
+        rows = np.full(n, -1, dtype=np.int64)
+        rows[ok] = indices[pos[ok]]
+        ok &= (rows >= 0) & (rows < pool.shape[0])
+        if not ok.any():
+            continue
+        cb = pool[rows[ok]]                         # [m, D], gathered through the list
+        S[b, :n][ok] = (cb @ qf[b].T).sum(axis=1)   # sum over d per head, then over heads
+        A[b, :n][ok] = (np.abs(cb) @ np.abs(qf[b]).T).sum(axis=1)
+    return S, A, n_slots
 
 
 def select_row(s: np.ndarray, nv: int, K: int, sorted_out: bool) -> np.ndarray:

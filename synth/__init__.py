@@ -71,6 +71,29 @@ class IndexerInputs:
 
 
 @dataclasses.dataclass
+class PagedInputs:
+    """One paged indexer batch: q[B,H,D], a pool c_pool[n_rows,D] and per-request
+    page lists indices[indptr[b]:indptr[b+1]] (CSR)."""
+    q: np.ndarray            # float32 or uint16 (bf16 bits)
+    c_pool: np.ndarray       # float32 or uint16 (bf16 bits)
+    indptr: np.ndarray       # int32 [B+1]
+    indices: np.ndarray      # int32 [indptr[B]]
+    max_pages: int
+    K: int
+    sorted: bool
+    dtype: str
+    name: str
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def H(self):
+        return self.q.shape[1]
+
+
+@dataclasses.dataclass
 class TopkInputs:
     scores: np.ndarray       # float32 [B, N]
     K: int
@@ -131,6 +154,40 @@ def make_integer_indexer(B, H, D, N_pad, seq_len, K, dtype, seed, lo=-3, hi=3,
                          sorted=False, dtype=dtype, name=name)
 
 
+# ---- paged centroid pools ("Iterate Centroids Score", benchmark protocol) -------------
+# page-count regimes N(mean, std) per request; the pages name the smallest and the
+# largest, and the three between are taken as the doublings in between
+PAGE_REGIMES = [(256, 64), (512, 128), (1024, 256), (2048, 512), (4096, 1024)]
+PAGED_BATCHES = [1, 4, 16, 32, 64]
+POOL_BLOCKS = 16384
+
+
+def make_paged(B, H, D, n_rows, pages, K, dtype, seed, sorted_out=False, max_pages=None,
+               name="custom"):
+    """q i.i.d. N(0,1); a pool of n_rows N(0,1) centroids; request b's page list is
+    pages[b] distinct pool rows drawn uniformly (lists of different requests may
+    share rows). pages: per-request counts, or (mean, std) of a normal regime
+    (rounded, clipped to [1, n_rows])."""
+    rng = np.random.default_rng(seed)
+    if isinstance(pages, tuple):
+        mu, sd = pages
+        counts = np.clip(np.rint(rng.normal(mu, sd, B)), 1, n_rows).astype(np.int64)
+    else:
+        counts = np.asarray(pages, dtype=np.int64)
+    q = _normal_f32(rng, (B, H, D))
+    pool = _normal_f32(rng, (n_rows, D))
+    lists = [rng.choice(n_rows, int(n), replace=False) for n in counts]
+    indptr = np.zeros(B + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum(counts)
+    indices = (np.concatenate(lists) if len(lists) else np.zeros(0)).astype(np.int32)
+    if dtype == "bf16":
+        q = f32_to_bf16_bits(q)
+        pool = f32_to_bf16_bits(pool)
+    mp = int(counts.max()) if max_pages is None else int(max_pages)
+    return PagedInputs(q=q, c_pool=pool, indptr=indptr.astype(np.int32), indices=indices,
+                       max_pages=mp, K=K, sorted=sorted_out, dtype=dtype, name=name)
+
+
 # ---- the distribution rotation of the top-K stress rows -------------------------------
 TOPK_DISTS = ["normal", "uniform", "lognormal", "zipf", "all_equal", "quant8",
               "sorted_asc", "sorted_desc", "normal_half_neginf"]
@@ -189,11 +246,12 @@ WORKLOADS = {
     3: "top-K stress: 64 rows x 30000 fp32, K=2048, 9-distribution rotation",
     4: "large GQA decode batch: B=128 H=16 D=128 bf16 N_pad=2048 K=256",
     5: "nearest-centroid assignment: 2^20 x 128 bf16 points, C=1024",
+    6: "paged pool: B=64 H=4 D=128 bf16, pages per request N(4096,1024) of 16384, K=256",
 }
 
 
 def workload(n: int, seed: int | None = None):
-    """Inputs of workload n (1..5), seeded with n unless a seed is given."""
+    """Inputs of workload n (1..6), seeded with n unless a seed is given."""
     s = n if seed is None else seed
     if n == 1:
         return make_indexer(1, 4, 128, 1024, [16384], 256, "f32", s, sorted_out=True,
@@ -214,4 +272,7 @@ def workload(n: int, seed: int | None = None):
                              K=256, sorted=False, dtype="bf16", name="w4_gqa_bf16")
     if n == 5:
         return make_assign(1 << 20, 1024, 128, s, name="w5_kmeans_assign")
+    if n == 6:
+        return make_paged(64, 4, 128, POOL_BLOCKS, PAGE_REGIMES[-1], 256, "bf16", s,
+                          name="w6_paged_bf16")
     raise ValueError(n)

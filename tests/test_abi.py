@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["idx_score", "idx_topk", "idx_select", "idx_assign", "idx_workspace_bytes",
+    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_assign",
+              "idx_workspace_bytes",
               "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
         assert n in names
 
@@ -120,6 +121,37 @@ def select_call(lib, **kw):
 ])
 def test_select_rejects(lib, kw, want):
     assert select_call(lib, **kw) == want
+
+
+def paged_call(lib, **kw):
+    a = dict(q=P, c=P, indptr=P, indices=P, ids=P, counts=None, scores_out=None, B=2, H=4, D=128,
+             n_rows=1000, n_indices=500, max_pages=300, K=10, dt=1, flags=0, ws=None,
+             ws_bytes=1 << 22)
+    a.update(kw)
+    return lib.idx_select_paged(a["q"], a["c"], a["indptr"], a["indices"], a["ids"], a["counts"],
+                                a["scores_out"], a["B"], a["H"], a["D"], a["n_rows"],
+                                a["n_indices"], a["max_pages"], a["K"], a["dt"], a["flags"],
+                                a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(c=None), INVALID), (dict(indptr=None), INVALID),
+    (dict(ids=None), INVALID), (dict(indices=None), INVALID), (dict(indptr=P + 2), INVALID),
+    (dict(indices=P + 1), INVALID), (dict(c=P + 8), INVALID), (dict(B=0), INVALID),
+    (dict(n_rows=0), INVALID), (dict(n_indices=-1), INVALID), (dict(max_pages=0), INVALID),
+    (dict(K=0), INVALID), (dict(dt=5), INVALID), (dict(flags=0x4), INVALID),
+    (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
+    (dict(B=16385, max_pages=4), UNSUPPORTED), (dict(ws=None), WORKSPACE),
+    (dict(ws=P, ws_bytes=100), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
+])
+def test_select_paged_rejects(lib, kw, want):
+    assert paged_call(lib, **kw) == want
+
+
+def test_select_paged_accepts_an_empty_index_list_without_a_pointer(lib):
+    # no list entries at all: a NULL list is legal; the call then fails only on
+    # the (missing) workspace, before any launch
+    assert paged_call(lib, indices=None, n_indices=0) == WORKSPACE
 
 
 def assign_call(lib, **kw):

@@ -168,6 +168,82 @@ def test_score_never_reads_masked_rows():
 
 
 # ----------------------------------------------------------------------------------------
+# paged scores: page lists into a shared pool
+# ----------------------------------------------------------------------------------------
+def test_score_paged_exact_against_rationals_through_the_lists():
+    """Brute force: each slot's exact rational score through its list entry."""
+    rng = np.random.default_rng(30)
+    B, H, D, R = 3, 2, 10, 9
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    pool = rng.standard_normal((R, D)).astype(np.float32)
+    indptr = np.array([0, 4, 4, 11])
+    indices = np.array([8, 0, 8, 3, 5, 1, 2, 7, 6, 4, 0])   # row 8 listed twice by request 0
+    S, A, n = oracle.score_paged(q, pool, indptr, indices, 6, "f32")
+    np.testing.assert_array_equal(n, [4, 0, 6])              # request 2 clamped to 6 slots
+    for b in range(B):
+        for i in range(6):
+            if i >= n[b]:
+                assert S[b, i] == -np.inf and A[b, i] == 0
+                continue
+            r = indices[indptr[b] + i]
+            exact = sum(Fraction(float(q[b, h, d])) * Fraction(float(pool[r, d]))
+                        for h in range(H) for d in range(D))
+            assert abs(Fraction(S[b, i]) - exact) <= Fraction(1e-15) * Fraction(A[b, i])
+    assert S[0, 0] == S[0, 2]                                # the same row scores the same
+
+
+def test_score_paged_one_hot_pool():
+    """Pool row j = alpha_j e_(j mod D), heads e_(i_h): s = alpha_row * #{h: i_h = row mod D}."""
+    D, R = 16, 40
+    alpha = np.arange(1, R + 1, dtype=np.float32)
+    pool = np.zeros((R, D), np.float32)
+    pool[np.arange(R), np.arange(R) % D] = alpha
+    heads = [[3, 3, 5], [0, 7, 7]]
+    q = np.zeros((2, 3, D), np.float32)
+    for b in range(2):
+        for h, i in enumerate(heads[b]):
+            q[b, h, i] = 1
+    indptr = np.array([0, 5, 9])
+    indices = np.array([3, 19, 35, 5, 0, 7, 23, 16, 39])
+    S, _, _ = oracle.score_paged(q, pool, indptr, indices, 5, "f32")
+    for b in range(2):
+        for i in range(indptr[b + 1] - indptr[b]):
+            r = indices[indptr[b] + i]
+            assert S[b, i] == alpha[r] * sum(1 for x in heads[b] if x == r % D)
+
+
+def test_score_paged_invalid_entries_and_missing_list_positions():
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 2, 8)).astype(np.float32)
+    pool = rng.standard_normal((5, 8)).astype(np.float32)
+    indptr = np.array([0, 4, 9])        # request 1 runs past the 7 list entries
+    indices = np.array([1, -1, 5, 4, 0, 2, 3])
+    S, A, n = oracle.score_paged(q, pool, indptr, indices, 5, "f32")
+    np.testing.assert_array_equal(n, [4, 5])
+    assert np.isfinite(S[0, [0, 3]]).all() and (S[0, [1, 2]] == -np.inf).all()
+    assert np.isfinite(S[1, :3]).all() and (S[1, 3:] == -np.inf).all()
+    assert (A[S == -np.inf] == 0).all()
+    ids, counts = oracle.select(S, n, 5, False)
+    np.testing.assert_array_equal(counts, [2, 3])
+    np.testing.assert_array_equal(ids[0], [0, 3, -1, -1, -1])
+
+
+def test_score_paged_identity_lists_reduce_to_dense_tables():
+    """Special case: lists that walk a per-request table in order are the dense
+    score of that table (the dense form is pinned by the closed forms above)."""
+    x = synth.make_indexer(3, 4, 32, 50, [50 * 16, 21 * 16 + 2, 0], 8, "bf16", 32, poison=False)
+    nv = oracle.n_valid(x.seq_len, 16, 50)
+    pool = x.c.reshape(3 * 50, 32)
+    indptr = np.concatenate([[0], np.cumsum(nv)])
+    indices = np.concatenate([b * 50 + np.arange(nv[b]) for b in range(3)])
+    S, A, n = oracle.score_paged(x.q, pool, indptr, indices, 50, "bf16")
+    Sd, Ad = oracle.score(x.q, x.c, x.seq_len, 16, "bf16")
+    np.testing.assert_array_equal(n, nv)
+    np.testing.assert_allclose(S, Sd, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(A, Ad, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------------------------------------
 # selection: brute force by rank, exhaustively on tiny rows
 # ----------------------------------------------------------------------------------------
 def _rank_select(s, nv, K, sorted_out):
