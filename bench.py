@@ -27,8 +27,9 @@ Prints one JSON line:
                         (alone, and followed by one arrival counter) on this GPU
 
 Other modes:
-  --workload N         1..6 (1: tiny fp32, 2: default, 3: top-K stress,
-                       4: large GQA batch, 5: k-means assignment, 6: paged pool)
+  --workload N         1..7 (1: tiny fp32, 2: default, 3: top-K stress,
+                       4: large GQA batch, 5: k-means assignment, 6: paged pool,
+                       7: prompt tokens)
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
   --parse-pmc DIR      turn rocprofv3 --pmc output into a traffic summary
 """
@@ -53,7 +54,8 @@ ROTATE_BYTES = 512 << 20
 CALIB_BYTES = 1 << 30
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
-          4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel"}
+          4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
+          7: "topk_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
            ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "api.cpp")]
 
@@ -189,6 +191,60 @@ class Paged:
                                  f"calls, median {med * 1e3:.1f} ms per call"
 
 
+class Prefill:
+    def __init__(self, x, torch, idx, copies):
+        self.x, self.torch, self.idx = x, torch, idx
+        q, c, p0 = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
+        self.inputs = [(q, c, p0)] + [(q.clone(), c.clone(), p0.clone()) for _ in range(copies - 1)]
+        dev = q.device
+        self.ids = torch.empty(x.B, x.T, x.K, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(x.B, x.T, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(idx.idx_prefill_workspace_bytes(x.B, x.T, x.N_pad, x.K, 0),
+                              dtype=torch.uint8, device=dev)
+        import numpy as np
+        ps = x.page_size
+        nv = [np.minimum(x.N_pad, (max(int(p), 0) + np.arange(x.T) + 1 + ps - 1) // ps)
+              for p in x.pos0]
+        self.units = int(sum(int(v.sum()) for v in nv))        # (token, visible block) pairs
+        rows = sum(int(v.max()) for v in nv)                    # centroid rows any token sees
+        # centroid rows read + query heads + pos0 + ids written (the per-token
+        # score rows are an intermediate and are not credited)
+        self.alg_bytes = rows * 256 + x.q.size * 2 + 4 * x.B + 4 * x.B * x.T * x.K
+        self.alg_flops = 2 * self.units * 128
+
+    def step(self, i, sorted=None):
+        q, c, p0 = self.inputs[i % len(self.inputs)]
+        self.idx.idx_select_prefill(q, c, p0, self.x.K, page_size=self.x.page_size,
+                                    sorted=self.x.sorted if sorted is None else sorted,
+                                    ids=self.ids, counts=self.counts, ws=self.ws)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][1]
+
+    def describe(self):
+        x = self.x
+        return {"workload": x.name, "call": "idx_select_prefill", "B": x.B, "T": x.T, "H": x.H,
+                "D": 128, "N_pad": x.N_pad, "pos0": [int(v) for v in x.pos0],
+                "page_size": x.page_size, "K": x.K, "sorted": x.sorted, "inputs": x.dtype,
+                "accumulate": "f32 (MFMA)", "token_block_pairs": self.units,
+                "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import oracle
+        x = self.x
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            S, _, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+            R = x.B * x.T
+            oracle.select(S.reshape(R, -1), NV.reshape(R), x.K, x.sorted)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        return self.units / med, f"the whole batch ({self.units} token-block pairs), " \
+                                 f"{len(times)} calls, median {med * 1e3:.1f} ms per call"
+
+
 class Topk:
     def __init__(self, x, torch, idx, copies):
         self.x, self.torch, self.idx = x, torch, idx
@@ -283,6 +339,8 @@ def make(w, torch, idx, copies):
         return Topk(x, torch, idx, copies)
     if w == 6:
         return Paged(x, torch, idx, copies)
+    if w == 7:
+        return Prefill(x, torch, idx, copies)
     return Assign(x, torch, idx, copies)
 
 
@@ -293,6 +351,8 @@ def input_bytes(w, x):
         return x.scores.nbytes
     if w == 6:
         return x.q.nbytes + x.c_pool.nbytes + x.indptr.nbytes + x.indices.nbytes
+    if w == 7:
+        return x.q.nbytes + x.c.nbytes
     return x.x.nbytes + x.c.nbytes
 
 
@@ -479,7 +539,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -590,7 +650,7 @@ def main():
         log("[bench] cold calls, host end-to-end, floors")
         extras["cold_us_per_call"] = stats_us(cold_times(torch, wl, 32))
         extras["host_e2e_us_per_call"] = stats_us(host_e2e_times(torch, wl, 32))
-        if a.workload in (2, 3, 4, 6):  # headline unsorted; the score-ordered output beside it
+        if a.workload in (2, 3, 4, 6, 7):  # headline unsorted; the score-ordered output beside it
             extras["sorted_us_per_call"] = min(graph_time(
                 torch, lambda i: wl.step(i, sorted=True), min(a.steps, 1000), 3)) * 1e3
         extras["floor"] = floors(torch, idx, wl, min(a.steps, 200))
@@ -609,7 +669,8 @@ def main():
     out = {
         "metric": METRIC,
         "value": wl.units * per_s,
-        "unit": {5: "points/s", 3: "entries/s", 6: "page slots/s"}.get(a.workload, "blocks/s"),
+        "unit": {5: "points/s", 3: "entries/s", 6: "page slots/s",
+                 7: "token-block pairs/s"}.get(a.workload, "blocks/s"),
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
         "launch": launch_desc,

@@ -13,7 +13,8 @@ import threading
 
 import torch
 
-__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_assign", "idx_workspace_bytes",
+__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
+           "idx_prefill_workspace_bytes", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
            "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
 
@@ -35,6 +36,9 @@ _SIGS = {
     "idx_select_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                   _c_int, ctypes.c_int64, _c_int, _c_int, _c_int, _u32, _vp,
                                   _c_size, _vp]),
+    "idx_prefill_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
+    "idx_select_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _u32, _vp, _c_size, _vp]),
     "idx_assign_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "idx_assign": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int64, _c_int, _c_int, _c_int, _vp,
                             _c_size, _vp]),
@@ -216,6 +220,34 @@ def idx_select_paged(q, c_pool, kv_indptr, kv_indices, K, max_pages, sorted=Fals
         _ptr(q), _ptr(c_pool), _ptr(kv_indptr), _ptr(kv_indices), _ptr(ids), _ptr(counts),
         _ptr(scores_out), B, H, D, n_rows, kv_indices.numel(), max_pages, K, _dtype_code(q),
         flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return ids, counts, scores_out
+
+
+def idx_prefill_workspace_bytes(B, T, N_pad, K, flags=0) -> int:
+    return load().idx_prefill_workspace_bytes(B, T, N_pad, K, flags)
+
+
+def idx_select_prefill(q, c, pos0, K, page_size=16, sorted=False, return_scores=False, ids=None,
+                       counts=None, scores_out=None, ws=None):
+    """Per-token scores and top-K of T prompt tokens per request (q [B,T,H,D],
+    c [B,N_pad,D], bf16). Returns (ids [B,T,K], counts [B,T], scores_out or None)."""
+    lib = load()
+    dev = _dev(q, c, pos0, ids, counts, scores_out, ws)
+    B, T, H, D = q.shape
+    N_pad = c.shape[1]
+    if ids is None:
+        ids = torch.empty(B, T, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, T, dtype=torch.int32, device=dev)
+    if return_scores and scores_out is None:
+        scores_out = torch.empty(B, T, N_pad, dtype=torch.float32, device=dev)
+    flags = IDX_SORTED if sorted else 0
+    nbytes = lib.idx_prefill_workspace_bytes(B, T, N_pad, K, flags)
+    if ws is None:
+        ws = _workspace(dev, nbytes, "prefill")
+    _check("idx_select_prefill", lib.idx_select_prefill(
+        _ptr(q), _ptr(c), _ptr(pos0), _ptr(ids), _ptr(counts), _ptr(scores_out), B, T, H, D,
+        N_pad, page_size, K, _dtype_code(q), flags, _ptr(ws), ws.numel(), _stream(dev)))
     return ids, counts, scores_out
 
 

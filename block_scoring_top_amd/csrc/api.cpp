@@ -177,6 +177,50 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
                                         kv_indices, n_indices, n_rows, stream));
 }
 
+size_t idx_prefill_workspace_bytes(int B, int T, int N_pad, int K, uint32_t flags) {
+  (void)K; (void)flags;
+  if (B < 1 || T < 1 || N_pad < 1) return 0;
+  const size_t rows = (size_t)B * T;
+  return round_up(rows * sizeof(int32_t), 256) + rows * stage_stride(N_pad) * sizeof(float);
+}
+
+int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_t* ids,
+                       int32_t* counts, float* scores_out, int B, int T, int H, int D, int N_pad,
+                       int page_size, int K, idx_dtype dt, uint32_t flags, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (q == nullptr || c == nullptr || pos0 == nullptr || ids == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(c, 16) || !aligned(pos0, 4) || !aligned(ids, 4) ||
+      !aligned(counts, 4) || !aligned(scores_out, 16))
+    return IDX_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || H < 1 || D < 1 || N_pad < 1 || page_size < 1 || K < 1)
+    return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if (flags & ~IDX_SORTED) return IDX_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)B * T;
+  if (rows > kMaxRows || rows * N_pad > (int64_t(1) << 40) || rows * K > kMaxRows ||
+      (int64_t)B * N_pad > kMaxRows)
+    return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_BF16 || H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
+  const bool sorted = (flags & IDX_SORTED) != 0;
+  if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
+  const size_t need = idx_prefill_workspace_bytes(B, T, N_pad, K, flags);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
+  int32_t* n_valid = static_cast<int32_t*>(ws);
+  float* scores = scores_out;
+  int64_t stride = N_pad;
+  if (scores == nullptr) {  // staged in the workspace, rows 16-byte aligned
+    scores = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                      round_up((size_t)rows * sizeof(int32_t), 256));
+    stride = stage_stride(N_pad);
+  }
+  int e = idxk::launch_prefill_score(q, c, pos0, scores, stride, n_valid, B, T, H, N_pad,
+                                     page_size, stream);
+  if (e != 0) return IDX_ERR_HIP;
+  return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, (int)rows, (int)stride, K,
+                                      sorted, stream));
+}
+
 // -|c|^2/2 per centroid, padded with -inf to a multiple of 128 (a whole number of
 // centroid tiles)
 size_t idx_assign_workspace_bytes(int C, int D) {

@@ -38,18 +38,19 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
 }
 
 // ---- idx_topk ----------------------------------------------------------------------------
-template <bool SORTED, bool BLOCKED>
-__global__ __launch_bounds__(kTopkNT) void topk_kernel(const float* __restrict__ scores,
-                                                       const int32_t* __restrict__ n_valid,
-                                                       int32_t* __restrict__ ids,
-                                                       int32_t* __restrict__ counts, int N,
-                                                       int K) {
-  __shared__ SelectSmem<kTopkNT, kTopkSlots> sm;
+// One workgroup of NT threads per row; rows longer than NT*SLOTS*4 keys are
+// streamed through the register tile.
+template <bool SORTED, int NT, int SLOTS>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ n_valid,
+                                                  int32_t* __restrict__ ids,
+                                                  int32_t* __restrict__ counts, int N, int K) {
+  __shared__ SelectSmem<NT, SLOTS> sm;
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<kTopkNT, kTopkSlots, SORTED, false, BLOCKED>(
+  select_row<NT, SLOTS, SORTED, false, false>(
       scores + (size_t)b * N, n, N, K, ids + (size_t)b * K, counts ? counts + b : nullptr, sm,
       sort_lds);
 }
@@ -145,17 +146,28 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
 
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
                 int B, int N, int K, bool sorted, void* stream) {
-  const dim3 grid((unsigned)B), block(kTopkNT);
+  const dim3 grid((unsigned)B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Rows come from HBM here, so they are read in the striped layout (every load
-  // fully coalesced); the blocked layout's strided loads cost more than its
-  // cheaper emit saves.
-  if (sorted)
-    hipLaunchKernelGGL((topk_kernel<true, false>), grid, block, sort_lds_bytes(K), s, scores,
-                       n_valid, ids, counts, N, K);
-  else
-    hipLaunchKernelGGL((topk_kernel<false, false>), grid, block, 0, s, scores, n_valid, ids,
-                       counts, N, K);
+  // fully coalesced). Many short rows (several rows per CU, each within one
+  // 256-thread register tile of 2048 keys) take 256-thread workgroups, so that
+  // several selects share a CU; otherwise 1024 threads per row. 256-thread
+  // workgroups order at most 1024 ids.
+  const bool narrow = B >= 512 && N <= 2048 && (!sorted || K <= 1024);
+  if (narrow) {
+    if (sorted)
+      hipLaunchKernelGGL((topk_kernel<true, 256, 2>), grid, dim3(256), sort_lds_bytes(K), s,
+                         scores, n_valid, ids, counts, N, K);
+    else
+      hipLaunchKernelGGL((topk_kernel<false, 256, 2>), grid, dim3(256), 0, s, scores, n_valid,
+                         ids, counts, N, K);
+  } else if (sorted) {
+    hipLaunchKernelGGL((topk_kernel<true, kTopkNT, kTopkSlots>), grid, dim3(kTopkNT),
+                       sort_lds_bytes(K), s, scores, n_valid, ids, counts, N, K);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<false, kTopkNT, kTopkSlots>), grid, dim3(kTopkNT), 0, s,
+                       scores, n_valid, ids, counts, N, K);
+  }
   return (int)hipGetLastError();
 }
 

@@ -165,6 +165,36 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
                      idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * idx_select_prefill -- per-token scores and top-K for T prompt tokens per
+ * request ("Round 15 Track C Audit", section 1 Target 1: the prompt path
+ * scores tiles of query tokens against the block keys with a matrix product,
+ * every token before its top-K; "Round 18 Track C", section 3: the score
+ * stage grows with the number of query tokens).
+ *   q    [B,T,H,D] bf16 (16-byte aligned): token t of request b sits at
+ *        position pos0[b] + t
+ *   c    [B,N_pad,D] bf16 (16-byte aligned): the request's block centroids
+ *   pos0 [B] int32 device array (negative values count as 0)
+ * Token t sees the blocks n < n_valid = min(N_pad, ceil((pos0[b] + t + 1) /
+ * page_size)) (the blocks up to the one holding itself), and
+ *   s[b,t,n] = sum_h q[b,t,h,:] . c[b,n,:] for those blocks, -inf past them.
+ * Each (b, t) row then gets the selection of idx_topk:
+ *   ids        [B,T,K] int32 output;  counts [B,T] int32 output or NULL
+ *   scores_out [B,T,N_pad] float32 output or NULL (16-byte aligned)
+ * The heads are summed per token in fp32 and split into two bf16 parts for
+ * the matrix cores (the dropped remainder is below 2^-16 of each summed
+ * value), products accumulated in fp32.
+ * dt == IDX_BF16, D == IDX_HEAD_DIM, H <= IDX_MAX_HEADS, K >= 1 (K <=
+ * IDX_MAX_SORTED_K with IDX_SORTED).
+ * ws / ws_bytes: at least idx_prefill_workspace_bytes(B, T, N_pad, K, flags)
+ * bytes (no zero-fill needed): per-token block counts and score staging.
+ */
+size_t idx_prefill_workspace_bytes(int B, int T, int N_pad, int K, uint32_t flags);
+int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_t* ids,
+                       int32_t* counts, float* scores_out, int B, int T, int H, int D, int N_pad,
+                       int page_size, int K, idx_dtype dt, uint32_t flags, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
  * idx_assign -- nearest-centroid k-means assignment ([KM] Summary): the select
  * step with K = 1 over a dense score matrix.
  *   assign[i] = argmax_j ( 2 * x[i,:].c[j,:] - |c[j,:]|^2 ), ties to the lower j,

@@ -18,6 +18,10 @@ sort, an argmax) as its only building blocks:
           lists into a shared pool of centroids ("Iterate Centroids Score",
           submission contract and benchmark protocol: the scorer reads a
           request's pages through its context, from a pool of 16384 blocks).
+  score_prefill  per-token scores of T prompt tokens, each token seeing the
+          blocks up to the one that holds it ("Round 15 Track C Audit",
+          section 1 Target 1: the prompt path scores tiles of query tokens
+          against the block keys before each token's top-K).
   select  the K highest-scoring valid blocks of each row, ties to the lower
           block id ("Iterate Topk": top-K indices from per-segment scores;
           "Round 18 Track C", section 2: ids compared exactly, with
@@ -45,8 +49,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_decode", "to_f64", "n_valid", "score", "score_paged", "select", "select_row",
-           "assign", "assign_scores"]
+__all__ = ["bf16_decode", "to_f64", "n_valid", "score", "score_paged", "score_prefill", "select",
+           "select_row", "assign", "assign_scores"]
 
 
 def bf16_decode(bits: np.ndarray) -> np.ndarray:
@@ -137,6 +141,38 @@ def score_paged(q, c_pool, indptr, indices, max_pages: int, dtype: str):
         S[b, :n][ok] = (cb @ qf[b].T).sum(axis=1)   # sum over d per head, then over heads
         A[b, :n][ok] = (np.abs(cb) @ np.abs(qf[b]).T).sum(axis=1)
     return S, A, n_slots
+
+
+def score_prefill(q, c, pos0, page_size: int, dtype: str):
+    """Per-token scores of prompt tokens in float64, their error scale and counts.
+
+    q [B,T,H,D], c [B,N_pad,D]. Token t of request b sits at position
+    pos0[b] + t (negative pos0 counts as 0) and sees the blocks n < n_valid(
+    pos0[b] + t + 1 tokens) -- the blocks up to the one that holds it (reading:
+    causal attention over the prompt, with the same block count rule as the
+    decode call).
+    Returns (S, A, NV): S, A float64 [B,T,N_pad] as in score(); NV int64 [B,T].
+    """
+    qf = to_f64(q, dtype)
+    B, T, H, D = qf.shape
+    N_pad = c.shape[1]
+    S = np.full((B, T, N_pad), -np.inf)
+    A = np.zeros((B, T, N_pad))
+    NV = np.zeros((B, T), dtype=np.int64)
+    for b in range(B):
+        p0 = max(int(pos0[b]), 0)
+        nv = n_valid(p0 + np.arange(T) + 1, page_size, N_pad)
+        NV[b] = nv
+        m = int(nv.max())
+        if m == 0:
+            continue
+        cb = to_f64(c[b, :m], dtype)                                   # [m, D]
+        per = (cb @ qf[b].reshape(T * H, D).T).reshape(m, T, H).sum(axis=2)      # [m, T]
+        per_abs = (np.abs(cb) @ np.abs(qf[b]).reshape(T * H, D).T).reshape(m, T, H).sum(axis=2)
+        for t in range(T):
+            S[b, t, :nv[t]] = per[:nv[t], t]
+            A[b, t, :nv[t]] = per_abs[:nv[t], t]
+    return S, A, NV
 
 
 def select_row(s: np.ndarray, nv: int, K: int, sorted_out: bool) -> np.ndarray:

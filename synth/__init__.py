@@ -188,6 +188,56 @@ def make_paged(B, H, D, n_rows, pages, K, dtype, seed, sorted_out=False, max_pag
                        max_pages=mp, K=K, sorted=sorted_out, dtype=dtype, name=name)
 
 
+# ---- prompt (prefill) tokens ("Round 15 Track C Audit", section 1 Target 1) -----------
+@dataclasses.dataclass
+class PrefillInputs:
+    """T prompt tokens per request: q[B,T,H,D], c[B,N_pad,D], pos0[B]."""
+    q: np.ndarray            # uint16 bf16 bits (or float32)
+    c: np.ndarray
+    pos0: np.ndarray         # int32 [B]
+    page_size: int
+    K: int
+    sorted: bool
+    dtype: str
+    name: str
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def T(self):
+        return self.q.shape[1]
+
+    @property
+    def H(self):
+        return self.q.shape[2]
+
+    @property
+    def N_pad(self):
+        return self.c.shape[1]
+
+
+def make_prefill(B, T, H, D, N_pad, pos0, K, seed, dtype="bf16", sorted_out=False,
+                 page_size=PAGE_SIZE, integer=False, name="custom"):
+    """q and c i.i.d. N(0,1) rounded to bf16 (or small integers); centroid rows
+    past the last token's block poisoned with a bf16 NaN."""
+    rng = np.random.default_rng(seed)
+    pos0 = np.asarray(pos0, dtype=np.int64)
+    if integer:
+        q = rng.integers(-3, 3, (B, T, H, D), endpoint=True).astype(np.float32)
+        c = rng.integers(-3, 3, (B, N_pad, D), endpoint=True).astype(np.float32)
+    else:
+        q = _normal_f32(rng, (B, T, H, D))
+        c = _normal_f32(rng, (B, N_pad, D))
+    if dtype == "bf16":
+        q = f32_to_bf16_bits(q)
+        c = f32_to_bf16_bits(c)
+        _poison_tail(c, np.maximum(pos0, 0) + T, page_size)
+    return PrefillInputs(q=q, c=c, pos0=pos0.astype(np.int32), page_size=page_size, K=K,
+                         sorted=sorted_out, dtype=dtype, name=name)
+
+
 # ---- the distribution rotation of the top-K stress rows -------------------------------
 TOPK_DISTS = ["normal", "uniform", "lognormal", "zipf", "all_equal", "quant8",
               "sorted_asc", "sorted_desc", "normal_half_neginf"]
@@ -247,11 +297,12 @@ WORKLOADS = {
     4: "large GQA decode batch: B=128 H=16 D=128 bf16 N_pad=2048 K=256",
     5: "nearest-centroid assignment: 2^20 x 128 bf16 points, C=1024",
     6: "paged pool: B=64 H=4 D=128 bf16, pages per request N(4096,1024) of 16384, K=256",
+    7: "prompt tokens: B=2 T=512 H=4 D=128 bf16, pos0 {4096, 30000}, N_pad=1920, K=256",
 }
 
 
 def workload(n: int, seed: int | None = None):
-    """Inputs of workload n (1..6), seeded with n unless a seed is given."""
+    """Inputs of workload n (1..7), seeded with n unless a seed is given."""
     s = n if seed is None else seed
     if n == 1:
         return make_indexer(1, 4, 128, 1024, [16384], 256, "f32", s, sorted_out=True,
@@ -275,4 +326,6 @@ def workload(n: int, seed: int | None = None):
     if n == 6:
         return make_paged(64, 4, 128, POOL_BLOCKS, PAGE_REGIMES[-1], 256, "bf16", s,
                           name="w6_paged_bf16")
+    if n == 7:
+        return make_prefill(2, 512, 4, 128, 1920, [4096, 30000], 256, s, name="w7_prefill_bf16")
     raise ValueError(n)

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_assign",
+    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
+              "idx_prefill_workspace_bytes", "idx_assign",
               "idx_workspace_bytes",
               "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
         assert n in names
@@ -152,6 +153,36 @@ def test_select_paged_accepts_an_empty_index_list_without_a_pointer(lib):
     # no list entries at all: a NULL list is legal; the call then fails only on
     # the (missing) workspace, before any launch
     assert paged_call(lib, indices=None, n_indices=0) == WORKSPACE
+
+
+def prefill_call(lib, **kw):
+    a = dict(q=P, c=P, pos0=P, ids=P, counts=None, scores_out=None, B=2, T=64, H=4, D=128,
+             N_pad=500, page_size=16, K=10, dt=1, flags=0, ws=None, ws_bytes=1 << 22)
+    a.update(kw)
+    return lib.idx_select_prefill(a["q"], a["c"], a["pos0"], a["ids"], a["counts"],
+                                  a["scores_out"], a["B"], a["T"], a["H"], a["D"], a["N_pad"],
+                                  a["page_size"], a["K"], a["dt"], a["flags"], a["ws"],
+                                  a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(c=None), INVALID), (dict(pos0=None), INVALID),
+    (dict(ids=None), INVALID), (dict(q=P + 8), INVALID), (dict(pos0=P + 2), INVALID),
+    (dict(scores_out=P + 4), INVALID), (dict(B=0), INVALID), (dict(T=0), INVALID),
+    (dict(N_pad=0), INVALID), (dict(page_size=0), INVALID), (dict(K=0), INVALID),
+    (dict(dt=3), INVALID), (dict(flags=0x100), INVALID), (dict(dt=0), UNSUPPORTED),
+    (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws=P, ws_bytes=64), WORKSPACE), (dict(ws=P + 64), WORKSPACE),
+])
+def test_select_prefill_rejects(lib, kw, want):
+    assert prefill_call(lib, **kw) == want
+
+
+def test_prefill_workspace_size(lib):
+    # per-token block counts (256-byte aligned), then B*T staged rows of round_up(N_pad, 4)
+    assert lib.idx_prefill_workspace_bytes(2, 64, 500, 10, 0) == 512 + 128 * 500 * 4
+    assert lib.idx_prefill_workspace_bytes(1, 3, 7, 10, 0) == 256 + 3 * 8 * 4
+    assert lib.idx_prefill_workspace_bytes(0, 3, 7, 10, 0) == 0
 
 
 def assign_call(lib, **kw):

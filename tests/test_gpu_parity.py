@@ -262,6 +262,20 @@ def test_topk_adversarial_rows(sorted_out):
         check_ids_exact(ids, counts, s, np.array(nv), K, sorted_out)
 
 
+@pytest.mark.parametrize("K,sorted_out", [(1, False), (300, False), (300, True), (1024, True),
+                                          (1100, True), (2000, False)])
+def test_topk_many_short_rows(K, sorted_out):
+    """600 rows of at most 2048 entries: 256-thread workgroups (1024-thread ones
+    when more than 1024 ids are to be ordered), every stress distribution."""
+    N = 1999 if sorted_out else 2048   # unaligned and aligned rows
+    x = synth.make_topk(600, N, K, 410 + K)
+    nv = np.random.default_rng(411).integers(0, N, 600)
+    nv[:3] = [0, 1, N]
+    say(f"[topk] many short rows K={K} sorted={sorted_out}")
+    ids, counts = run_topk(x.scores, K, nv, sorted_out)
+    check_ids_exact(ids, counts, x.scores, nv, K, sorted_out)
+
+
 @pytest.mark.parametrize("N", [1, 3, 1000, 32768, 32769, 70001])
 def test_topk_lengths(N):
     x = synth.make_topk(9, N, 300, 401 + N)

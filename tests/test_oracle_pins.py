@@ -244,6 +244,50 @@ def test_score_paged_identity_lists_reduce_to_dense_tables():
 
 
 # ----------------------------------------------------------------------------------------
+# prompt (prefill) tokens: each token sees the blocks up to its own
+# ----------------------------------------------------------------------------------------
+def test_score_prefill_block_counts_by_hand():
+    """Page 4, first token at position 5: tokens at positions 5..12 see 6..13
+    tokens, i.e. 2, 2, 2, 3, 3, 3, 3, 4 blocks; capped at N_pad = 3 for the rest."""
+    q = np.ones((1, 8, 1, 4), np.float32)
+    c = np.ones((1, 3, 4), np.float32)
+    S, _, NV = oracle.score_prefill(q, c, [5], 4, "f32")
+    np.testing.assert_array_equal(NV[0], [2, 2, 2, 3, 3, 3, 3, 3])
+    for t in range(8):
+        assert np.isfinite(S[0, t, :NV[0, t]]).all() and (S[0, t, NV[0, t]:] == -np.inf).all()
+    _, _, NV0 = oracle.score_prefill(q, c, [-7], 4, "f32")    # negative start counts as 0
+    np.testing.assert_array_equal(NV0[0], [1, 1, 1, 1, 2, 2, 2, 2])
+
+
+def test_score_prefill_exact_against_rationals():
+    rng = np.random.default_rng(40)
+    B, T, H, D, N = 2, 5, 3, 6, 4
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    c = rng.standard_normal((B, N, D)).astype(np.float32)
+    S, A, NV = oracle.score_prefill(q, c, [0, 9], 4, "f32")
+    for b in range(B):
+        for t in range(T):
+            for n in range(N):
+                if n >= NV[b, t]:
+                    assert S[b, t, n] == -np.inf and A[b, t, n] == 0
+                    continue
+                exact = sum(Fraction(float(q[b, t, h, d])) * Fraction(float(c[b, n, d]))
+                            for h in range(H) for d in range(D))
+                assert abs(Fraction(S[b, t, n]) - exact) <= Fraction(1e-15) * Fraction(A[b, t, n])
+
+
+def test_score_prefill_each_token_is_a_decode_call():
+    """Special case: token t alone is the decode score of a request holding
+    pos0 + t + 1 tokens (the decode form is pinned by the closed forms above)."""
+    x = synth.make_prefill(2, 9, 4, 32, 40, [17, 300], 8, 41)
+    S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, 16, "bf16")
+    for t in range(9):
+        Sd, Ad = oracle.score(x.q[:, t], x.c, x.pos0.astype(np.int64) + t + 1, 16, "bf16")
+        np.testing.assert_allclose(S[:, t], Sd, rtol=1e-13, atol=0)
+        np.testing.assert_allclose(A[:, t], Ad, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------------------------------------
 # selection: brute force by rank, exhaustively on tiny rows
 # ----------------------------------------------------------------------------------------
 def _rank_select(s, nv, K, sorted_out):
