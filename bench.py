@@ -29,7 +29,7 @@ Prints one JSON line:
 Other modes:
   --workload N         1..7 (1: tiny fp32, 2: default, 3: top-K stress,
                        4: large GQA batch, 5: k-means assignment, 6: paged pool,
-                       7: prompt tokens)
+                       7: prompt tokens, 8: pooled keys)
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
   --parse-pmc DIR      turn rocprofv3 --pmc output into a traffic summary
 """
@@ -55,7 +55,7 @@ CALIB_BYTES = 1 << 30
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
-          7: "topk_kernel"}
+          7: "topk_kernel", 8: "pool_keys_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
            ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "api.cpp")]
 
@@ -245,6 +245,51 @@ class Prefill:
                                  f"{len(times)} calls, median {med * 1e3:.1f} ms per call"
 
 
+class Pool:
+    def __init__(self, x, torch, idx, copies):
+        self.x, self.torch, self.idx = x, torch, idx
+        k, sl = to_dev(x.k), to_dev(x.seq_len)
+        self.inputs = [(k, sl)] + [(k.clone(), sl.clone()) for _ in range(copies - 1)]
+        self.c = torch.zeros(x.B, x.N_pad, 128, dtype=k.dtype, device=k.device)
+        import numpy as np
+        S_pad = x.k.shape[1]
+        sl_np = np.clip(x.seq_len.astype(np.int64), 0, S_pad)
+        nv = np.minimum(x.N_pad, (sl_np + x.page_size - 1) // x.page_size)
+        tokens = int(np.minimum(sl_np, nv * x.page_size).sum())
+        elem = 2 if x.dtype == "bf16" else 4
+        self.units = int(nv.sum())                               # blocks pooled
+        # keys of the tokens held + one centroid row per block + seq_len
+        self.alg_bytes = tokens * 128 * elem + self.units * 128 * elem + 4 * x.B
+        self.alg_flops = tokens * 128
+
+    def step(self, i, sorted=None):
+        k, sl = self.inputs[i % len(self.inputs)]
+        self.idx.idx_pool_keys(k, sl, self.x.N_pad, self.x.page_size, c=self.c)
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][0]
+
+    def describe(self):
+        x = self.x
+        return {"workload": x.name, "call": "idx_pool_keys", "B": x.B, "S_pad": int(x.k.shape[1]),
+                "D": 128, "N_pad": x.N_pad, "page_size": x.page_size, "inputs": x.dtype,
+                "seq_len": [int(v) for v in x.seq_len], "blocks": self.units,
+                "input_copies": len(self.inputs)}
+
+    def cpu_oracle(self, budget_s):
+        import oracle
+        x = self.x
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            oracle.pool_keys(x.k, x.seq_len, x.N_pad, x.page_size, x.dtype)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        return self.units / med, f"the whole batch ({self.units} blocks), {len(times)} calls, " \
+                                 f"median {med * 1e3:.1f} ms per call"
+
+
 class Topk:
     def __init__(self, x, torch, idx, copies):
         self.x, self.torch, self.idx = x, torch, idx
@@ -341,6 +386,8 @@ def make(w, torch, idx, copies):
         return Paged(x, torch, idx, copies)
     if w == 7:
         return Prefill(x, torch, idx, copies)
+    if w == 8:
+        return Pool(x, torch, idx, copies)
     return Assign(x, torch, idx, copies)
 
 
@@ -353,6 +400,8 @@ def input_bytes(w, x):
         return x.q.nbytes + x.c_pool.nbytes + x.indptr.nbytes + x.indices.nbytes
     if w == 7:
         return x.q.nbytes + x.c.nbytes
+    if w == 8:
+        return x.k.nbytes
     return x.x.nbytes + x.c.nbytes
 
 
@@ -539,7 +588,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -670,7 +719,7 @@ def main():
         "metric": METRIC,
         "value": wl.units * per_s,
         "unit": {5: "points/s", 3: "entries/s", 6: "page slots/s",
-                 7: "token-block pairs/s"}.get(a.workload, "blocks/s"),
+                 7: "token-block pairs/s", 8: "blocks pooled/s"}.get(a.workload, "blocks/s"),
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
         "launch": launch_desc,

@@ -14,7 +14,7 @@ import threading
 import torch
 
 __all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
-           "idx_prefill_workspace_bytes", "idx_assign", "idx_workspace_bytes",
+           "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
            "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
 
@@ -36,6 +36,8 @@ _SIGS = {
     "idx_select_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                   _c_int, ctypes.c_int64, _c_int, _c_int, _c_int, _u32, _vp,
                                   _c_size, _vp]),
+    "idx_pool_keys": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               _vp]),
     "idx_prefill_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
     "idx_select_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _u32, _vp, _c_size, _vp]),
@@ -221,6 +223,20 @@ def idx_select_paged(q, c_pool, kv_indptr, kv_indices, K, max_pages, sorted=Fals
         _ptr(scores_out), B, H, D, n_rows, kv_indices.numel(), max_pages, K, _dtype_code(q),
         flags, _ptr(ws), ws.numel(), _stream(dev)))
     return ids, counts, scores_out
+
+
+def idx_pool_keys(k, seq_len, N_pad, page_size=16, c=None):
+    """Block centroids: c[b,n] = mean of the keys k[b, tokens of block n]
+    (k [B,S_pad,128], float32 or bf16). Rows past a request's blocks are not
+    written (a new c is zero-filled)."""
+    lib = load()
+    dev = _dev(k, seq_len, c)
+    B, S_pad, D = k.shape
+    if c is None:
+        c = torch.zeros(B, N_pad, D, dtype=k.dtype, device=dev)
+    _check("idx_pool_keys", lib.idx_pool_keys(_ptr(k), _ptr(seq_len), _ptr(c), B, S_pad, D, N_pad,
+                                              page_size, _dtype_code(k), _stream(dev)))
+    return c
 
 
 def idx_prefill_workspace_bytes(B, T, N_pad, K, flags=0) -> int:

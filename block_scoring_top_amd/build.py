@@ -22,7 +22,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-I", os.path.join(ROOT, "include")]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
 
-HIP_SOURCES = ["indexer.hip", "assign.hip", "prefill.hip", "floor.hip"]
+HIP_SOURCES = ["indexer.hip", "assign.hip", "prefill.hip", "pool.hip", "floor.hip"]
 # assign.hip's inputs are finite by contract; without NaN semantics its running
 # max compiles to plain 3-input maxes (no per-operand canonicalisation)
 EXTRA_FLAGS = {"assign.hip": ["-fno-honor-nans"]}

@@ -177,6 +177,18 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
                                         kv_indices, n_indices, n_rows, stream));
 }
 
+int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_pad, int D,
+                  int N_pad, int page_size, idx_dtype dt, void* stream) {
+  if (k == nullptr || seq_len == nullptr || c == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(c, 16) || !aligned(seq_len, 4)) return IDX_ERR_INVALID_ARG;
+  if (B < 1 || S_pad < 1 || D < 1 || N_pad < 1 || page_size < 1) return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if ((int64_t)B * S_pad > kMaxRows || (int64_t)B * N_pad > kMaxRows) return IDX_ERR_INVALID_ARG;
+  if (D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
+  return hip_status(idxk::launch_pool_keys(k, seq_len, c, B, S_pad, N_pad, page_size,
+                                           dt == IDX_BF16, stream));
+}
+
 size_t idx_prefill_workspace_bytes(int B, int T, int N_pad, int K, uint32_t flags) {
   (void)K; (void)flags;
   if (B < 1 || T < 1 || N_pad < 1) return 0;

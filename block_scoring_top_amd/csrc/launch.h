@@ -27,6 +27,10 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
 int launch_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C,
                   float* cnorm, void* stream);
 
+// Block means of the keys: c[b,n,:] = mean of k[b, tokens of block n, :].
+int launch_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_pad, int N_pad,
+                     int page_size, bool bf16, void* stream);
+
 // Prefill scores of T tokens per request into scores[(b*T + t) * row_stride + n]
 // (row_stride >= N_pad) and each token's visible block count into n_valid[b*T + t].
 int launch_prefill_score(const void* q, const void* c, const int32_t* pos0, float* scores,

@@ -165,6 +165,24 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
                      idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * idx_pool_keys -- block centroids from the keys ("Round 15 Track C Audit",
+ * section 2: the pooled keys are a stage of the indexer checked for parity;
+ * [CS]: the scorer reads one centroid per block). Reading: a block's pooled
+ * key is the mean of the keys of its tokens.
+ *   k       [B,S_pad,D] keys (16-byte aligned), token s of request b in row s
+ *   seq_len [B] int32 device array: request b holds tokens 0 .. seq_len[b]-1
+ *           (clamped to [0, S_pad])
+ *   c       [B,N_pad,D] output, same dtype as k (16-byte aligned)
+ *   c[b,n,:] = mean of k[b,s,:] over s in [n*page_size, min((n+1)*page_size,
+ *              seq_len[b])), for n < min(N_pad, ceil(seq_len[b]/page_size));
+ * rows past that count are not written. Sums in fp32 in token order, then a
+ * correctly rounded division; bf16 output rounds the fp32 mean to nearest even.
+ * D == IDX_HEAD_DIM, dt IDX_F32 or IDX_BF16. No workspace.
+ */
+int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_pad, int D,
+                  int N_pad, int page_size, idx_dtype dt, void* stream);
+
+/*
  * idx_select_prefill -- per-token scores and top-K for T prompt tokens per
  * request ("Round 15 Track C Audit", section 1 Target 1: the prompt path
  * scores tiles of query tokens against the block keys with a matrix product,

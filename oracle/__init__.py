@@ -7,6 +7,9 @@ It is a plain, slow, obviously correct restatement of what the indexer
 computes, in float64 numpy with library primitives (a matrix product, a stable
 sort, an argmax) as its only building blocks:
 
+  pool_keys  c[b,n,:] = mean of the keys of the tokens of block n ("Round 15
+          Track C Audit", section 2: the pooled keys are a stage of the indexer;
+          reading: a block's pooled key is the mean of its tokens' keys).
   score   s[b,n] = sum_h sum_d q[b,h,d] * c[b,n,d] for every block n that holds
           tokens of request b; blocks past the request's last token are -inf.
           ("Iterate Centroids Score": the indexer's scorer rates each request's
@@ -49,8 +52,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_decode", "to_f64", "n_valid", "score", "score_paged", "score_prefill", "select",
-           "select_row", "assign", "assign_scores"]
+__all__ = ["bf16_decode", "to_f64", "n_valid", "pool_keys", "score", "score_paged",
+           "score_prefill", "select", "select_row", "assign", "assign_scores"]
 
 
 def bf16_decode(bits: np.ndarray) -> np.ndarray:
@@ -76,6 +79,29 @@ def n_valid(seq_len, page_size: int, n_pad: int) -> np.ndarray:
     """
     s = np.asarray(seq_len, dtype=np.int64)
     return np.minimum(n_pad, (s + page_size - 1) // page_size)
+
+
+def pool_keys(k, seq_len, n_pad: int, page_size: int, dtype: str):
+    """Block means of the keys in float64, and the absolute means (error scale).
+
+    k [B, S_pad, D]; request b holds tokens 0 .. seq_len[b]-1 (clamped to
+    [0, S_pad]). For n < n_valid: C[b,n] = mean of k[b,s] over the tokens s of
+    block n, s in [n*page_size, min((n+1)*page_size, seq_len[b])); M[b,n] = the
+    mean of |k[b,s]|. Rows past n_valid are NaN (not produced).
+    Returns (C, M, nv).
+    """
+    kf = to_f64(k, dtype)
+    B, S_pad, D = kf.shape
+    sl = np.clip(np.asarray(seq_len, dtype=np.int64), 0, S_pad)
+    nv = n_valid(sl, page_size, n_pad)
+    C = np.full((B, n_pad, D), np.nan)
+    M = np.full((B, n_pad, D), np.nan)
+    for b in range(B):
+        for n in range(int(nv[b])):
+            toks = kf[b, n * page_size:min((n + 1) * page_size, int(sl[b]))]
+            C[b, n] = toks.mean(axis=0)
+            M[b, n] = np.abs(toks).mean(axis=0)
+    return C, M, nv
 
 
 def score(q, c, seq_len, page_size: int, dtype: str):

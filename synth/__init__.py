@@ -188,6 +188,36 @@ def make_paged(B, H, D, n_rows, pages, K, dtype, seed, sorted_out=False, max_pag
                        max_pages=mp, K=K, sorted=sorted_out, dtype=dtype, name=name)
 
 
+# ---- keys of the cache, pooled into block centroids -----------------------------------
+@dataclasses.dataclass
+class KeysInputs:
+    """Keys k[B,S_pad,D] of B requests holding seq_len[b] tokens each."""
+    k: np.ndarray            # float32 or uint16 (bf16 bits)
+    seq_len: np.ndarray      # int32 [B]
+    N_pad: int
+    page_size: int
+    dtype: str
+    name: str
+
+    @property
+    def B(self):
+        return self.k.shape[0]
+
+
+def make_keys(B, S_pad, D, N_pad, seq_len, dtype, seed, page_size=PAGE_SIZE, name="custom"):
+    """Keys i.i.d. N(0,1) (rounded to bf16); token rows past a request's length
+    poisoned with a bf16 NaN."""
+    rng = np.random.default_rng(seed)
+    k = _normal_f32(rng, (B, S_pad, D))
+    seq_len = np.asarray(seq_len, dtype=np.int64)
+    if dtype == "bf16":
+        k = f32_to_bf16_bits(k)
+        for b, sl in enumerate(seq_len):
+            k[b, max(int(sl), 0):] = BF16_POISON
+    return KeysInputs(k=k, seq_len=seq_len.astype(np.int32), N_pad=N_pad, page_size=page_size,
+                      dtype=dtype, name=name)
+
+
 # ---- prompt (prefill) tokens ("Round 15 Track C Audit", section 1 Target 1) -----------
 @dataclasses.dataclass
 class PrefillInputs:
@@ -298,11 +328,12 @@ WORKLOADS = {
     5: "nearest-centroid assignment: 2^20 x 128 bf16 points, C=1024",
     6: "paged pool: B=64 H=4 D=128 bf16, pages per request N(4096,1024) of 16384, K=256",
     7: "prompt tokens: B=2 T=512 H=4 D=128 bf16, pos0 {4096, 30000}, N_pad=1920, K=256",
+    8: "pooled keys: B=4 bf16 keys, seq_len {4096, 16384, 65536, 131072}, 16-token blocks",
 }
 
 
 def workload(n: int, seed: int | None = None):
-    """Inputs of workload n (1..7), seeded with n unless a seed is given."""
+    """Inputs of workload n (1..8), seeded with n unless a seed is given."""
     s = n if seed is None else seed
     if n == 1:
         return make_indexer(1, 4, 128, 1024, [16384], 256, "f32", s, sorted_out=True,
@@ -328,4 +359,7 @@ def workload(n: int, seed: int | None = None):
                           name="w6_paged_bf16")
     if n == 7:
         return make_prefill(2, 512, 4, 128, 1920, [4096, 30000], 256, s, name="w7_prefill_bf16")
+    if n == 8:
+        return make_keys(4, 131072, 128, 8192, [4096, 16384, 65536, 131072], "bf16", s,
+                         name="w8_pool_keys_bf16")
     raise ValueError(n)

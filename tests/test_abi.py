@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared()
     for n in ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
-              "idx_prefill_workspace_bytes", "idx_assign",
+              "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign",
               "idx_workspace_bytes",
               "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
         assert n in names
@@ -183,6 +183,24 @@ def test_prefill_workspace_size(lib):
     assert lib.idx_prefill_workspace_bytes(2, 64, 500, 10, 0) == 512 + 128 * 500 * 4
     assert lib.idx_prefill_workspace_bytes(1, 3, 7, 10, 0) == 256 + 3 * 8 * 4
     assert lib.idx_prefill_workspace_bytes(0, 3, 7, 10, 0) == 0
+
+
+def pool_call(lib, **kw):
+    a = dict(k=P, seq_len=P, c=P, B=2, S_pad=1000, D=128, N_pad=63, page_size=16, dt=1)
+    a.update(kw)
+    return lib.idx_pool_keys(a["k"], a["seq_len"], a["c"], a["B"], a["S_pad"], a["D"], a["N_pad"],
+                             a["page_size"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(k=None), INVALID), (dict(seq_len=None), INVALID), (dict(c=None), INVALID),
+    (dict(k=P + 8), INVALID), (dict(c=P + 4), INVALID), (dict(seq_len=P + 1), INVALID),
+    (dict(B=0), INVALID), (dict(S_pad=0), INVALID), (dict(N_pad=0), INVALID),
+    (dict(page_size=0), INVALID), (dict(dt=9), INVALID), (dict(D=64), UNSUPPORTED),
+    (dict(B=1 << 20, S_pad=1 << 12), INVALID),
+])
+def test_pool_keys_rejects(lib, kw, want):
+    assert pool_call(lib, **kw) == want
 
 
 def assign_call(lib, **kw):

@@ -288,6 +288,39 @@ def test_score_prefill_each_token_is_a_decode_call():
 
 
 # ----------------------------------------------------------------------------------------
+# pooled keys: block means
+# ----------------------------------------------------------------------------------------
+def test_pool_keys_closed_forms():
+    """An arithmetic progression of keys has its midpoint as block mean; a
+    partial last block averages only the tokens held; constant keys pool to
+    themselves."""
+    S_pad, D = 40, 4
+    tok = np.arange(S_pad, dtype=np.float32)
+    k = np.stack([np.stack([tok, 2 * tok, np.full(S_pad, 3.0), -tok], axis=1)] * 2).astype(np.float32)
+    C, M, nv = oracle.pool_keys(k, [37, 16], 10, 8, "f32")
+    np.testing.assert_array_equal(nv, [5, 2])
+    # request 0: blocks of tokens 0..7, 8..15, 16..23, 24..31 and 32..36
+    for n, (lo, hi) in enumerate([(0, 8), (8, 16), (16, 24), (24, 32), (32, 37)]):
+        mid = (lo + hi - 1) / 2
+        np.testing.assert_array_equal(C[0, n], [mid, 2 * mid, 3.0, -mid])
+        np.testing.assert_array_equal(M[0, n], [mid, 2 * mid, 3.0, mid])
+    assert np.isnan(C[0, 5:]).all() and np.isnan(C[1, 2:]).all()
+
+
+def test_pool_keys_exact_against_rationals_and_clamps():
+    rng = np.random.default_rng(50)
+    k = rng.standard_normal((2, 13, 5)).astype(np.float32)
+    C, _, nv = oracle.pool_keys(k, [13, 99], 4, 3, "f32")   # 99 tokens clamp to the 13 held
+    np.testing.assert_array_equal(nv, [4, 4])               # ceil(13/3) = 5 blocks, capped at 4
+    for b in range(2):
+        for n in range(4):
+            toks = range(3 * n, min(3 * n + 3, 13))
+            for d in range(5):
+                exact = sum(Fraction(float(k[b, s, d])) for s in toks) / len(toks)
+                assert abs(Fraction(C[b, n, d]) - exact) <= Fraction(1e-15) * (abs(exact) + 1)
+
+
+# ----------------------------------------------------------------------------------------
 # selection: brute force by rank, exhaustively on tiny rows
 # ----------------------------------------------------------------------------------------
 def _rank_select(s, nv, K, sorted_out):
