@@ -48,10 +48,9 @@ struct SelectSmem {
   static constexpr int NW = NT / kWave;
   static constexpr int E = SLOTS * NW;  // emit-count entries per tile
   uint32_t hist[2][kBins];
-  uint32_t wsum[4];
   uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
   uint32_t wmin[NW], wmax[NW];  // per-wave min / max of a pass's active keys
-  uint32_t sel_bin, sel_need, sel_tot, n_cand;
+  uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
 };
@@ -386,7 +385,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
   constexpr int E = SLOTS * NW;
-  static_assert(NT >= 256 && NT % 256 == 0, "the bin scan uses the first 256 threads");
+  static_assert(NT >= 256 && NT % 256 == 0, "at least four waves; histogram clears use waves 1..");
+  static_assert(kBins == 32 * kWave, "the bin search gives each lane of wave 0 32 bins");
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
@@ -410,7 +410,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
 
   // Each pass histograms the next digit of the keys that still match the
   // resolved prefix, then finds the bin holding the need-th largest of them:
-  // thread t < 256 owns bins [kBins - 8(t+1), kBins - 8t), scanned from the top.
+  // wave 0 scans the bins from the top (see below).
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
   int level = 0;  // digits resolved (kPasses = the whole key)
   bool take_all = false;
@@ -443,39 +443,56 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       sm.wmax[w] = kmax;
     }
     __syncthreads();
-    // read before the next barrier: the next pass rewrites these slots
-    for (int ww = 0; ww < NW; ++ww) {
-      kmin = sm.wmin[ww] < kmin ? sm.wmin[ww] : kmin;
-      kmax = sm.wmax[ww] > kmax ? sm.wmax[ww] : kmax;
-    }
-    uint32_t c8[8], loc = 0, incl = 0;
-    if (t < 256) {
-      const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 8 * (t + 1));
-      const uint4 lo = hv[0], hi = hv[1];
-      c8[0] = hi.w; c8[1] = hi.z; c8[2] = hi.y; c8[3] = hi.x;  // descending bins
-      c8[4] = lo.w; c8[5] = lo.z; c8[6] = lo.y; c8[7] = lo.x;
+    // Wave 0 alone finds the bin: lane l owns the 32 bins [kBins - 32(l+1),
+    // kBins - 32l), read from the top down, and one wave scan of the lanes'
+    // totals gives the counts above each lane. It also reduces the per-wave
+    // key ranges. The other waves clear the next pass's histogram meanwhile.
+    if (w == 0) {
+      const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
+      uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) loc += c8[k];
-      incl = wave_incl_scan(loc);
-      if (lane == kWave - 1) sm.wsum[w] = incl;
-    }
-    for (int i = t; i < kBins; i += NT) sm.hist[buf ^ 1][i] = 0u;
-    __syncthreads();
-    if (t < 256) {
-      for (int ww = 0; ww < w; ++ww) incl += sm.wsum[ww];
+      for (int j = 0; j < 8; ++j) {
+        const uint4 v = hv[7 - j];
+        g8[j] = v.x + v.y + v.z + v.w;
+      }
+      uint32_t loc = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) loc += g8[j];
+      const uint32_t incl = wave_incl_scan(loc);
+      if (p == 0 && lane == kWave - 1) sm.n_cand = incl;
       uint32_t cum = incl - loc;
-      if (p == 0 && t == 255) sm.n_cand = incl;
-      if (cum < need && need <= incl) {
+      if (cum < need && need <= incl) {  // one lane: the need-th key is in its bins
+        int jj = 0;
+        uint32_t before = cum;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (cum < need && need <= cum + c8[k]) {
-            sm.sel_bin = (uint32_t)(kBins - 1 - 8 * t - k);
-            sm.sel_need = need - cum;
-            sm.sel_tot = c8[k];
+        for (int j = 0; j < 8; ++j) {
+          if (cum < need && need <= cum + g8[j]) {
+            jj = j;
+            before = cum;
           }
-          cum += c8[k];
+          cum += g8[j];
+        }
+        const uint4 v = hv[7 - jj];
+        const uint32_t c4[4] = {v.w, v.z, v.y, v.x};
+        cum = before;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (cum < need && need <= cum + c4[k]) {
+            sm.sel_bin = (uint32_t)(kBins - 1 - 32 * lane - 4 * jj - k);
+            sm.sel_need = need - cum;
+            sm.sel_tot = c4[k];
+          }
+          cum += c4[k];
         }
       }
+      uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
+      uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
+      lo = wave_reduce_minmax<true>(lo);
+      hi = wave_reduce_minmax<false>(hi);
+      if (lane == 0) sm.all_same = lo == hi ? 1u : 0u;
+      if (lane == 0) sm.same_key = lo;
+    } else {
+      for (int i = t - kWave; i < kBins; i += NT - kWave) sm.hist[buf ^ 1][i] = 0u;
     }
     __syncthreads();
     if (p == 0) {
@@ -487,8 +504,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     }
     // every active key is the same value: the threshold is that key, of which
     // `need` are taken (identical keys would only fill one bin per later pass)
-    if (kmin == kmax) {
-      prefix = kmin;
+    if (sm.all_same) {
+      prefix = sm.same_key;
       level = kPasses;
       break;
     }
