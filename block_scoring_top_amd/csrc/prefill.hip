@@ -67,86 +67,103 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
   // blocks visible to the tile's last token bound every token of the tile
   const int nv_max = prefill_n_valid(p0, min(t0 + kPfTok, T) - 1, page_size, N_pad);
   float* out = scores + (size_t)b * T * row_stride;
-  if (n0 >= N_pad) return;
-  if (n0 >= nv_max) {  // nothing visible in this column block: -inf for every token
+  // columns no token of the tile sees get -inf; a workgroup with none visible
+  // at all leaves at once (the condition is the same for all its waves)
+  auto fill_dead = [&]() {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      const int n = n0 + col;
-      if (t < T && n < N_pad) out[(size_t)t * row_stride + n] = -__builtin_inff();
+      if (t < T && n0 + col < N_pad) out[(size_t)t * row_stride + n0 + col] = -__builtin_inff();
     }
+  };
+  if (ct * kPfCols >= nv_max) {
+    fill_dead();
     return;
   }
+  const bool live = n0 < nv_max;  // this wave's 32 columns hold a visible block
 
   // B operand: centroid row n0 + col (clamped in range; discarded past N_pad),
-  // 8 dims of each 16-dim k-step
+  // 8 dims of each 16-dim k-step; issued first, it lands while q_bar is built
   uint4 cb[8];
-  {
+  if (live) {
     const int n = min(n0 + col, N_pad - 1);
     const uint4* cr = reinterpret_cast<const uint4*>(c + ((size_t)b * N_pad + n) * kHeadDim);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) cb[ks] = cr[2 * ks + half];
   }
 
-  // A operand: q_bar of token t0 + col (zero past T), split into bf16 hi + lo
-  uint32_t hi[8][4], lo[8][4];
-  {
-    const int t = t0 + col;
-    float s[8][8];
+  // A operand, built once per workgroup in LDS: item (token u, 16-byte chunk k)
+  // of the tile sums the token's H heads over 8 dims (16 consecutive lanes read
+  // one head row of a token: 256 contiguous bytes), splits the sum into bf16
+  // hi + lo, and stores both at slot k * 32 + u, so that a wave's operand read
+  // (32 tokens, one chunk) is 512 contiguous bytes.
+  __shared__ uint4 a_hi[16 * kPfTok], a_lo[16 * kPfTok];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+  for (int it = 0; it < 16 * kPfTok / kPfNT; ++it) {
+    const int item = it * kPfNT + threadIdx.x;
+    const int u = item >> 4, k = item & 15;
+    const int t = t0 + u;
+    float sum[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[ks][e] = 0.f;
+    for (int e = 0; e < 8; ++e) sum[e] = 0.f;
     if (t < T) {
-      const uint16_t* qt = q + ((size_t)b * T + t) * H * kHeadDim;
-      for (int h = 0; h < H; ++h) {
-        const uint4* qr = reinterpret_cast<const uint4*>(qt + (size_t)h * kHeadDim);
+      const uint4* qt = reinterpret_cast<const uint4*>(q + ((size_t)b * T + t) * H * kHeadDim) + k;
+      // four heads per step: their loads are in flight together
+      for (int h0 = 0; h0 < H; h0 += 4) {
+        uint4 v[4];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint4 v = qr[2 * ks + half];
-          const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < 4; ++i) v[i] = qt[(size_t)(h0 + i < H ? h0 + i : H - 1) * 16];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            s[ks][2 * k] += bf16_lo(wd[k]);
-            s[ks][2 * k + 1] += bf16_hi(wd[k]);
+        for (int i = 0; i < 4; ++i) {
+          if (h0 + i >= H) break;
+          const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sum[2 * e] += bf16_lo(wd[e]);
+            sum[2 * e + 1] += bf16_hi(wd[e]);
           }
         }
       }
     }
+    uint32_t h4[4], l4[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t h0 = bf16_rne_bits(s[ks][2 * k]), h1 = bf16_rne_bits(s[ks][2 * k + 1]);
-        const float r0 = s[ks][2 * k] - __uint_as_float(h0 << 16);
-        const float r1 = s[ks][2 * k + 1] - __uint_as_float(h1 << 16);
-        hi[ks][k] = h0 | (h1 << 16);
-        lo[ks][k] = bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t h0 = bf16_rne_bits(sum[2 * e]), h1 = bf16_rne_bits(sum[2 * e + 1]);
+      const float r0 = sum[2 * e] - __uint_as_float(h0 << 16);
+      const float r1 = sum[2 * e + 1] - __uint_as_float(h1 << 16);
+      h4[e] = h0 | (h1 << 16);
+      l4[e] = bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
     }
+    a_hi[k * kPfTok + u] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+    a_lo[k * kPfTok + u] = make_uint4(l4[0], l4[1], l4[2], l4[3]);
   }
+  __syncthreads();
 
+  if (!live) {
+    fill_dead();
+    return;
+  }
   pf_f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const pf_bf16x8 bv = __builtin_bit_cast(pf_bf16x8, cb[ks]);
-    const pf_bf16x8 ah = __builtin_bit_cast(pf_bf16x8, make_uint4(hi[ks][0], hi[ks][1], hi[ks][2], hi[ks][3]));
-    const pf_bf16x8 al = __builtin_bit_cast(pf_bf16x8, make_uint4(lo[ks][0], lo[ks][1], lo[ks][2], lo[ks][3]));
+    const pf_bf16x8 ah = __builtin_bit_cast(pf_bf16x8, a_hi[(2 * ks + half) * kPfTok + col]);
+    const pf_bf16x8 al = __builtin_bit_cast(pf_bf16x8, a_lo[(2 * ks + half) * kPfTok + col]);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
   }
 
-  // value r of this lane: token t0 + 8(r/4) + 4 half + r%4, centroid n0 + col
+  // value r of this lane: token t0 + 8(r/4) + 4 half + r%4, centroid n0 + col.
+  // Block n is visible to token t iff it starts at or before the token:
+  // n * page_size <= pos0 + t (the same as n < ceil((pos0 + t + 1) / page_size)).
+  const int n = n0 + col;
+  const int64_t start = (int64_t)n * page_size - p0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    const int n = n0 + col;
-    if (t < T && n < N_pad) {
-      const int nv = prefill_n_valid(p0, t, page_size, N_pad);
-      out[(size_t)t * row_stride + n] = n < nv ? acc[r] : -__builtin_inff();
-    }
+    if (t < T && n < N_pad) out[(size_t)t * row_stride + n] = start <= t ? acc[r] : -__builtin_inff();
   }
 }
 
