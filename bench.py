@@ -57,7 +57,8 @@ KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
           7: "topk_kernel", 8: "pool_keys_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
-           ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "api.cpp")]
+           ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "prefill.hip",
+            "pool.hip", "api.cpp")]
 
 
 def source_digest() -> str:
