@@ -148,6 +148,18 @@ def test_select_multi_tile_rows():
     full_select_check(x, 500, True)
 
 
+def test_select_maximum_requests_and_heads():
+    """The largest request count one call takes (16384, one arrival line each)
+    with short tables, and the largest head count (64)."""
+    rng = np.random.default_rng(320)
+    seq = rng.integers(0, 40 * 16, 16384)
+    seq[:3] = [0, 1, 40 * 16]
+    x = synth.make_indexer(16384, 2, 128, 40, seq, 9, "bf16", 320)
+    full_select_check(x, 9, False)
+    x = synth.make_indexer(3, 64, 128, 3000, [3000 * 16, 1500 * 16 + 5, 16], 100, "bf16", 321)
+    full_select_check(x, 100, True)
+
+
 def test_select_constant_centroids_tie_to_lowest_ids():
     x = synth.make_indexer(2, 4, 128, 600, [600 * 16, 333 * 16], 50, "f32", 302)
     x.c[:] = x.c[:, :1, :]  # every block has the same centroid: all scores tie
