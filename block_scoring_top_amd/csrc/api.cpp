@@ -88,8 +88,9 @@ int idx_score(const void* q, const void* c, const int32_t* seq_len, float* score
 }
 
 size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags) {
-  (void)B; (void)N; (void)K; (void)flags;
-  return 0;
+  (void)flags;
+  if (B < 1 || N < 1 || K < 1) return 0;
+  return idxk::topk_split_workspace_bytes(B, N, K);
 }
 
 int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts, int B,
@@ -103,8 +104,10 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
   const bool sorted = (flags & IDX_SORTED) != 0;
   if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
   const size_t need = idx_topk_workspace_bytes(B, N, K, flags);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return IDX_ERR_WORKSPACE;
-  return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted, stream));
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
+    return IDX_ERR_WORKSPACE;
+  return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted,
+                                      need > 0 ? ws : nullptr, stream));
 }
 
 // largest score-ordered K that 256-thread workgroups sort (four ids per thread)
@@ -230,7 +233,7 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
                                      page_size, stream);
   if (e != 0) return IDX_ERR_HIP;
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, (int)rows, (int)stride, K,
-                                      sorted, stream));
+                                      sorted, nullptr, stream));
 }
 
 // -|c|^2/2 per centroid, padded with -inf to a multiple of 128 (a whole number of

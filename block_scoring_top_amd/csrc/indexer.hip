@@ -11,6 +11,8 @@ constexpr int kScoreNT = 256;   // idx_score workgroup: 4 waves
 // One arrival counter per request, each on its own 128-byte line: the atomics of
 // one line are serialised where they are performed, so requests must not share.
 constexpr int kTicketStride = 32;
+// arrival lines of B rows, rounded to 256 bytes
+size_t topk_ticket_bytes(int B) { return ((size_t)B * kTicketStride * 4 + 255) / 256 * 256; }
 constexpr int kTopkNT = 1024;   // top-K workgroup: 16 waves
 constexpr int kTopkSlots = 8;   // register tile: 1024*8*4 = 32768 keys
 
@@ -51,8 +53,56 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
   select_row<NT, SLOTS, SORTED, false, false>(
-      scores + (size_t)b * N, n, N, K, ids + (size_t)b * K, counts ? counts + b : nullptr, sm,
-      sort_lds);
+      scores + (size_t)b * N, n, N, K, IdsOut{ids + (size_t)b * K}, counts ? counts + b : nullptr,
+      sm, sort_lds);
+}
+
+// Long rows, few of them: each row is cut into S segments of L entries (L a
+// multiple of 4), one workgroup per segment. A segment's workgroup selects its
+// own top-K and hands them over as (score, index) candidates; the last of the
+// row's segments to arrive selects the row's top-K from the S*K candidates.
+// The global top-K is inside the union of the segments' top-Ks (the same total
+// order on each side), and candidates are laid out in segment order, each
+// segment's in ascending index order, so candidate order is index order and
+// the lower-index tie-break carries over.
+// Workspace per row: an arrival line, and cstride >= S*K candidate scores and
+// ids (cstride a multiple of 4).
+template <bool SORTED>
+__global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_valid,
+    int32_t* __restrict__ ids, int32_t* __restrict__ counts, int N, int K, int S, int L,
+    uint32_t* tickets, float* cand_score, int32_t* cand_id, int cstride) {
+  __shared__ SelectSmem<kTopkNT, kTopkSlots> sm;
+  __shared__ int s_last;
+  extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
+  const int b = blockIdx.x / S;
+  const int seg = blockIdx.x - b * S;
+  int n = N;
+  if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
+  const int lo = seg * L;
+  const int seg_n = max(0, min(lo + L, n) - lo);
+  float* rs = cand_score + (size_t)b * cstride;
+  int32_t* ri = cand_id + (size_t)b * cstride;
+  select_row<kTopkNT, kTopkSlots, false, false, false>(
+      scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K,
+      CandOut{rs + (size_t)seg * K, ri + (size_t)seg * K, lo}, nullptr, sm, sort_lds);
+  // hand-off: as in the fused select (agent-scope stores, all memory operations
+  // of the workgroup complete, one relaxed agent-scope ticket)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&tickets[(size_t)b * kTicketStride], 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == (uint32_t)(S - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  select_row<kTopkNT, kTopkSlots, SORTED, true, false>(
+      rs, S * K, cstride, K, MappedIdsOut{ids + (size_t)b * K, ri}, counts ? counts + b : nullptr,
+      sm, sort_lds);
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
@@ -124,7 +174,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   if (threadIdx.x == 0)  // ready for the next call on this workspace
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  select_row<NT, SLOTS, SORTED, true, BLOCKED>(row, nv, row_cap, K, ids + (size_t)b * K,
+  select_row<NT, SLOTS, SORTED, true, BLOCKED>(row, nv, row_cap, K, IdsOut{ids + (size_t)b * K},
                                       counts ? counts + b : nullptr, sm, sort_lds,
                                       scores_out != nullptr ? nullptr : row);
 }
@@ -144,10 +194,37 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
   return (int)hipGetLastError();
 }
 
+int topk_segments(int B, int N, int K) {
+  // more workgroups while a row's segments stay long (at least 4096 entries and
+  // twice K) and the candidates fit one register tile of the merge
+  int S = 1;
+  while (S < 8 && (int64_t)B * S * 2 <= 512 && N / (S * 2) >= 4096 && N / (S * 2) >= 2 * K &&
+         (int64_t)(S * 2) * K <= kTopkNT * kTopkSlots * 4)
+    S *= 2;
+  return S;
+}
+
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
-                int B, int N, int K, bool sorted, void* stream) {
+                int B, int N, int K, bool sorted, void* split_ws, void* stream) {
   const dim3 grid((unsigned)B);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int S = split_ws != nullptr ? topk_segments(B, N, K) : 1;
+  if (S > 1) {
+    const int L = ((N + S - 1) / S + 3) / 4 * 4;
+    const int cstride = (S * K + 3) / 4 * 4;
+    char* w = static_cast<char*>(split_ws);
+    uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
+    float* cs = reinterpret_cast<float*>(w + topk_ticket_bytes(B));
+    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_ticket_bytes(B) + (size_t)B * cstride * 4);
+    const dim3 g2((unsigned)((int64_t)B * S));
+    if (sorted)
+      hipLaunchKernelGGL((topk_split_kernel<true>), g2, dim3(kTopkNT), sort_lds_bytes(K), s,
+                         scores, n_valid, ids, counts, N, K, S, L, tickets, cs, ci, cstride);
+    else
+      hipLaunchKernelGGL((topk_split_kernel<false>), g2, dim3(kTopkNT), 0, s, scores, n_valid,
+                         ids, counts, N, K, S, L, tickets, cs, ci, cstride);
+    return (int)hipGetLastError();
+  }
   // Rows come from HBM here, so they are read in the striped layout (every load
   // fully coalesced). Many short rows (several rows per CU, each within one
   // 256-thread register tile of 2048 keys) take 256-thread workgroups, so that
@@ -169,6 +246,13 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
                        scores, n_valid, ids, counts, N, K);
   }
   return (int)hipGetLastError();
+}
+
+size_t topk_split_workspace_bytes(int B, int N, int K) {
+  const int S = topk_segments(B, N, K);
+  if (S <= 1) return 0;
+  const size_t cstride = ((size_t)S * K + 3) / 4 * 4;
+  return topk_ticket_bytes(B) + (size_t)B * cstride * 8;
 }
 
 int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,

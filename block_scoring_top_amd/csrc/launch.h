@@ -11,8 +11,12 @@ namespace idxk {
 int launch_score(const void* q, const void* c, const int32_t* seq_len, float* scores, int B,
                  int H, int N_pad, int page_size, bool bf16, int chunk, void* stream);
 
+// split_ws: NULL (one workgroup per row), or at least topk_split_workspace_bytes
+// of zero-filled workspace (long rows are then cut into segments selected by
+// several workgroups, merged by the last one; the workspace is left zeroed).
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
-                int B, int N, int K, bool sorted, void* stream);
+                int B, int N, int K, bool sorted, void* split_ws, void* stream);
+size_t topk_split_workspace_bytes(int B, int N, int K);
 
 // indptr == nullptr: dense tables (c is [B, N_pad, 128], seq_len gives the
 // valid rows). Otherwise paged: c is a pool of n_rows centroids, request b's

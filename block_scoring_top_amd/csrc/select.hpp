@@ -350,12 +350,56 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int P, uint64_t* 
   }
 }
 
-// Sorts the m pairs in sortbuf[0..m) into descending order and writes the low
-// words, inverted, to ids_out[0..m): E = 1 up to NT pairs (one per thread),
-// else P / NT per thread.
-template <int NT, int E>
-__device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
-                                                int32_t* ids_out) {
+// Where select_row puts its result: put(pos, id, key) for the pos-th selected
+// entry (its index in the row and its order key), pad(k) for the unused slots
+// k in [m, K).
+//
+// IdsOut: the ids themselves, -1 in unused slots.
+struct IdsOut {
+  int32_t* ids;
+  __device__ __forceinline__ void put(int pos, int id, uint32_t) const { ids[pos] = id; }
+  __device__ __forceinline__ void pad(int k) const { ids[k] = -1; }
+};
+
+// score of an order key (the inverse of order_key; -0.0 comes back as +0.0)
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// CandOut: the candidates of one segment of a row, as (score, row index) pairs,
+// written with agent-scope stores for the workgroup that merges the segments;
+// unused slots hold -inf (never selected).
+struct CandOut {
+  float* score;
+  int32_t* id;
+  int base;  // the segment's first index in the row
+  __device__ __forceinline__ void put(int pos, int i, uint32_t key) const {
+    __hip_atomic_store(score + pos, key_to_score(key), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(id + pos, base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void pad(int k) const {
+    __hip_atomic_store(score + k, -__builtin_inff(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(id + k, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+// MappedIdsOut: selecting over a candidate list, the id of candidate i is
+// map[i] (written by other workgroups: read with agent-scope loads).
+struct MappedIdsOut {
+  int32_t* ids;
+  const int32_t* map;
+  __device__ __forceinline__ void put(int pos, int i, uint32_t) const {
+    ids[pos] = __hip_atomic_load(map + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void pad(int k) const { ids[k] = -1; }
+};
+
+// Sorts the m pairs in sortbuf[0..m) into descending order and hands each
+// entry (its position i in the order, its row index from the inverted low
+// word) to out.put: E = 1 up to NT pairs (one per thread), else P / NT per
+// thread.
+template <int NT, int E, typename Out>
+__device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P, const Out& out) {
   const int t = threadIdx.x;
   __syncthreads();  // every pair is in sortbuf
   uint64_t v[E];
@@ -368,7 +412,7 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = E * t + e;
-    if (i < m) ids_out[i] = (int32_t)~(uint32_t)v[e];
+    if (i < m) out.put(i, (int32_t)~(uint32_t)v[e], (uint32_t)(v[e] >> 32));
   }
 }
 
@@ -376,9 +420,9 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
 // BLOCKED: the caller guarantees n <= NT * SLOTS * 4; the row is held in the
 // blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
 // when it does not fit one register tile).
-template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED>
+template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut>
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
-                                                         int32_t* ids_out, int32_t* count_out,
+                                                         const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
                                                          uint64_t* sortbuf,
                                                          float* stage_zero = nullptr) {
@@ -560,7 +604,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           if constexpr (SORTED) {
             sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
           } else {
-            ids_out[pos] = id;
+            out.put((int)pos, id, keys[i][j]);
           }
         }
         gb += gt ? 1u : 0u;
@@ -623,7 +667,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           if constexpr (SORTED) {
             sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
           } else {
-            ids_out[pos] = id;
+            out.put((int)pos, id, keys[i][j]);
           }
         }
         gb += gt[j] ? 1u : 0u;
@@ -634,7 +678,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     carry_eq += sm.tot_eq;
   }
 
-  for (int k = (int)m_out + t; k < K; k += NT) ids_out[k] = -1;
+  for (int k = (int)m_out + t; k < K; k += NT) out.pad(k);
   if (count_out != nullptr && t == 0) *count_out = (int32_t)m_out;
 
   if constexpr (SORTED) {
@@ -643,13 +687,13 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     int P = 2;
     while (P < (int)m_out) P <<= 1;
     if (P <= NT) {
-      sort_pairs_desc<NT, 1>(sortbuf, (int)m_out, P, ids_out);
+      sort_pairs_desc<NT, 1>(sortbuf, (int)m_out, P, out);
     } else if (P == 2 * NT) {
-      sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, ids_out);
+      sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, out);
     } else {
       // P == 4 * NT: callers give 256-thread workgroups at most 1024 ids to
       // order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
-      sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, ids_out);
+      sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, out);
     }
   }
   if (stage_zero != nullptr) {

@@ -109,8 +109,13 @@ int idx_score(const void* q, const void* c, const int32_t* seq_len, float* score
  *   scores  [B,N] float32 (16-byte aligned)      n_valid [B] int32 or NULL
  *   ids     [B,K] int32 output                    counts  [B] int32 output or NULL
  * B >= 1, N >= 1, K >= 1 (K <= IDX_MAX_SORTED_K with IDX_SORTED).
- * ws / ws_bytes: workspace of at least idx_topk_workspace_bytes() bytes (may be
- * NULL when that is 0).
+ * ws / ws_bytes: workspace of at least idx_topk_workspace_bytes() bytes
+ * (256-byte aligned; may be NULL when that is 0). It is nonzero when rows are
+ * few and long: each row is then cut into segments selected by several
+ * workgroups and merged by the last to finish (arrival counters and segment
+ * candidates live in the workspace). It must be zero-filled before first use;
+ * every call returns it to that state, so it may serve any later call that
+ * fits it. Calls that may overlap (other streams) need distinct workspaces.
  */
 size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags);
 int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,

@@ -67,6 +67,21 @@ def test_workspace_sizes(lib):
     assert lib.idx_assign_workspace_bytes(1031, 128) == 1152 * 4
 
 
+def test_topk_workspace_sizes(lib):
+    # few long rows: arrival lines (256-byte aligned) + B * round_up(S*K, 4) candidate
+    # scores and ids; here S = 4 segments (64 rows x 30000, K = 2048)
+    assert lib.idx_topk_workspace_bytes(64, 30000, 2048, 0) == 64 * 128 + 64 * 8192 * 8
+    assert lib.idx_topk_workspace_bytes(1000, 30000, 10, 0) == 0   # enough rows already
+    assert lib.idx_topk_workspace_bytes(64, 2000, 10, 0) == 0       # short rows
+    assert lib.idx_topk_workspace_bytes(0, 30000, 10, 0) == 0
+
+
+def test_topk_long_rows_require_the_workspace(lib):
+    assert topk_call(lib, B=64, N=30000, K=2048) == WORKSPACE
+    assert topk_call(lib, B=64, N=30000, K=2048, ws=P, ws_bytes=100) == WORKSPACE
+    assert topk_call(lib, B=64, N=30000, K=2048, ws=P + 16, ws_bytes=1 << 30) == WORKSPACE
+
+
 def score_call(lib, **kw):
     a = dict(q=P, c=P, seq_len=P, scores=P, B=1, H=4, D=128, N_pad=64, page_size=16, dt=1)
     a.update(kw)

@@ -288,6 +288,23 @@ def test_topk_many_short_rows(K, sorted_out):
     check_ids_exact(ids, counts, x.scores, nv, K, sorted_out)
 
 
+@pytest.mark.parametrize("K,sorted_out", [(1, False), (777, True), (4096, True), (6000, False)])
+def test_topk_long_rows_split_into_segments(K, sorted_out):
+    """Few long rows: several workgroups per row select segments, the last one
+    merges; lengths end inside, at and just past segment boundaries, ties across
+    segments (all-equal and quantised rows) go to the lower index."""
+    B, N = 20, 50000
+    x = synth.make_topk(B, N, K, 420 + K)
+    nv = np.random.default_rng(421).integers(0, N, B)
+    nv[:7] = [0, 1, N, 12500, 12501, 12499, 25000]
+    say(f"[topk] split rows K={K} sorted={sorted_out}")
+    ids, counts = run_topk(x.scores, K, nv, sorted_out)
+    check_ids_exact(ids, counts, x.scores, nv, K, sorted_out)
+    ids2, counts2 = run_topk(x.scores, K, nv, sorted_out)   # the workspace is reusable
+    np.testing.assert_array_equal(ids2, ids)
+    np.testing.assert_array_equal(counts2, counts)
+
+
 @pytest.mark.parametrize("N", [1, 3, 1000, 32768, 32769, 70001])
 def test_topk_lengths(N):
     x = synth.make_topk(9, N, 300, 401 + N)
