@@ -176,11 +176,11 @@ __device__ __forceinline__ void load_keys_blocked(const float* row, int n, int c
   }
 }
 
-// Adds one count per active lane to h[digit]. When every active lane of the
-// wave has the same digit (all-equal or sorted rows) the wave adds them with one
-// atomic; when the first active lane's digit is shared by at least 16 lanes that
-// group is added with one atomic and the rest one by one; otherwise every lane
-// adds its own count (distinct digits do not serialise).
+// Adds one count per active lane to h[digit]. When the first active lane's
+// digit is shared by at least 16 lanes (all-equal, sorted or quantised rows),
+// that lane adds the whole group's count and the group's other lanes add
+// nothing, in the same atomic instruction as the lanes of other digits;
+// otherwise every lane adds its own count.
 __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t digit) {
   const uint64_t m = ballot(act);
   if (m == 0) return;
@@ -189,8 +189,8 @@ __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t digit) 
   const uint64_t same = ballot(act && digit == d0);
   const uint32_t ns = popc64(same);
   if (ns >= 16) {
-    if (lane_id() == leader) atomicAdd(&h[d0], ns);
-    if (same != m && act && digit != d0) atomicAdd(&h[digit], 1u);
+    const bool is_leader = lane_id() == leader;
+    if (act && (digit != d0 || is_leader)) atomicAdd(&h[digit], is_leader ? ns : 1u);
   } else if (act) {
     atomicAdd(&h[digit], 1u);
   }
