@@ -53,7 +53,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 ROTATE_BYTES = 512 << 20
 CALIB_BYTES = 1 << 30
 
-KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_kernel",
+KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_split_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
           7: "topk_kernel", 8: "pool_keys_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
