@@ -29,7 +29,7 @@ int chunk_rows(int B, int N_pad, uint32_t flags, int lo, int target) {
 // idx_score: 256-thread workgroups, 16 rows per step, ~1024 of them (4 per CU)
 constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
 // idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~256 of
-// them: one per CU, all resident at once); many requests -> 256-thread
+// them: one per CU, all resident at once); many requests -> 512-thread
 // workgroups (16 rows per step, ~1024)
 constexpr int kWideMaxRequests = 32;
 constexpr int kWideChunkMin = 64, kWideTarget = 256;
@@ -110,7 +110,8 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
                                       need > 0 ? ws : nullptr, stream));
 }
 
-// largest score-ordered K that 256-thread workgroups sort (four ids per thread)
+// largest score-ordered K that the many-request workgroups (512 threads) sort
+// (kept at four ids per thread of a 256-thread workgroup)
 constexpr int kNarrowMaxSortedK = 1024;
 
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {
@@ -135,7 +136,7 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
   uint32_t* tickets = static_cast<uint32_t*>(ws);
   float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
-  // 1024-thread workgroups for a few requests, 256-thread ones for many; the
+  // 1024-thread workgroups for a few requests, 512-thread ones for many; the
   // score order of more than 1024 ids is sorted by 1024-thread workgroups only
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
   const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)

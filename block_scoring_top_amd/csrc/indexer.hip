@@ -264,9 +264,9 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
   const dim3 grid((unsigned)B * nchunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // wide: 1024-thread workgroups (16 waves keep the selecting workgroup's SIMDs
-  // busy; for a few long requests); otherwise 256 threads (many requests)
-  // blocked: every row fits the select's register tile (1024*2*4 = 256*8*4 = 8192;
-  // 256-thread workgroups use 2 slots, 256*2*4 = 2048, when that is enough)
+  // busy; for a few long requests); otherwise 512 threads (many requests)
+  // blocked: every row fits the select's register tile (1024*2*4 = 512*4*4 = 8192;
+  // 512-thread workgroups use 1 slot, 512*1*4 = 2048, when that is enough)
   const bool blocked = N_pad <= 8192;
   const bool short_rows = N_pad <= 2048;
   const bool paged = indptr != nullptr;
@@ -288,9 +288,9 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
     if (blocked) IDX_LAUNCH_FUSED(BF, SO, 1024, 2, true);                            \
     else IDX_LAUNCH_FUSED(BF, SO, 1024, 2, false);                                   \
   } else {                                                                           \
-    if (short_rows) IDX_LAUNCH_FUSED(BF, SO, 256, 2, true);                          \
-    else if (blocked) IDX_LAUNCH_FUSED(BF, SO, 256, 8, true);                        \
-    else IDX_LAUNCH_FUSED(BF, SO, 256, 8, false);                                    \
+    if (short_rows) IDX_LAUNCH_FUSED(BF, SO, 512, 1, true);                          \
+    else if (blocked) IDX_LAUNCH_FUSED(BF, SO, 512, 4, true);                        \
+    else IDX_LAUNCH_FUSED(BF, SO, 512, 4, false);                                    \
   }
   if (bf16) {
     if (sorted) { IDX_LAUNCH_FUSED_NT(true, true); }

@@ -691,8 +691,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     } else if (P == 2 * NT) {
       sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, out);
     } else {
-      // P == 4 * NT: callers give 256-thread workgroups at most 1024 ids to
-      // order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
+      // P == 4 * NT: callers give 256- and 512-thread workgroups at most 1024
+      // ids to order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
       sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, out);
     }
   }
