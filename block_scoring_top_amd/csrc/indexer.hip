@@ -160,8 +160,8 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   // agent-scope (write-through) stores; waiting for every outstanding memory
   // operation of this wave, then a workgroup barrier, means all of them have
   // completed before the ticket is taken. The last of the request's n_part
-  // chunks to take a ticket reads the row with agent-scope loads and returns
-  // the staged row to zero.
+  // chunks to take a ticket reads the row with agent-scope loads (the staged
+  // row is scratch: every call writes the entries it reads).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -175,8 +175,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   select_row<NT, SLOTS, SORTED, true, BLOCKED>(row, nv, row_cap, K, IdsOut{ids + (size_t)b * K},
-                                      counts ? counts + b : nullptr, sm, sort_lds,
-                                      scores_out != nullptr ? nullptr : row);
+                                      counts ? counts + b : nullptr, sm, sort_lds);
 }
 
 // ---- launchers ---------------------------------------------------------------------------

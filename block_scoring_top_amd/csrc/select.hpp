@@ -47,9 +47,9 @@ template <int NT, int SLOTS>
 struct SelectSmem {
   static constexpr int NW = NT / kWave;
   static constexpr int E = SLOTS * NW;  // emit-count entries per tile
-  uint32_t hist[2][kBins];
+  alignas(16) uint32_t hist[2][kBins];
   uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
-  uint32_t wmin[NW], wmax[NW];  // per-wave min / max of a pass's active keys
+  uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the row's active keys
   uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
@@ -416,7 +416,6 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
   }
 }
 
-// stage_zero (may be null): the row is returned to zero at the end.
 // BLOCKED: the caller guarantees n <= NT * SLOTS * 4; the row is held in the
 // blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
 // when it does not fit one register tile).
@@ -424,8 +423,7 @@ template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename 
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
                                                          const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
-                                                         uint64_t* sortbuf,
-                                                         float* stage_zero = nullptr) {
+                                                         uint64_t* sortbuf) {
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
   constexpr int E = SLOTS * NW;
@@ -449,6 +447,34 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   else if (cached)
     load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
 
+  // The all-equal exits need the min and max of the keys in play: after the
+  // first pass those of the row (blocked rows take them here, once, and the
+  // max may include inactive keys: kKeyNegInf is below every active key but
+  // negative NaNs, so min == max still means all active keys are equal), and
+  // for striped rows (idx_topk inputs: quantised, heavy-tailed or tied rows)
+  // after the second pass those of the keys left in the chosen bins. The
+  // blocked rows of the fused select (dot-product scores) skip that second
+  // range: its cost on every row outweighs the pass it saves on tied rows,
+  // and the third pass resolves every remaining bit either way.
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (BLOCKED) {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (!slot_live(0, i)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = keys[i][j];
+        kmin = min(kmin, key == kKeyNegInf ? 0xFFFFFFFFu : key);
+        kmax = max(kmax, key);
+      }
+    }
+    kmin = wave_reduce_minmax<true>(kmin);
+    kmax = wave_reduce_minmax<false>(kmax);
+    if (lane == 0) {
+      sm.wmin[w] = kmin;
+      sm.wmax[w] = kmax;
+    }
+  }
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
   __syncthreads();
 
@@ -464,7 +490,11 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     const int shift = digit_shift(p);
     const uint32_t dmask = digit_mask(p);
     const int hshift = p == 0 ? 0 : digit_shift(p - 1);  // the resolved bits sit above this
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // over this pass's active keys
+    const bool track = !BLOCKED && p <= 1;  // this pass takes the range of its keys
+    if (p == 1) {
+      kmin = 0xFFFFFFFFu;
+      kmax = 0u;
+    }
     for (int tile = 0; tile < ntiles; ++tile) {
       if (!cached) load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
 #pragma unroll
@@ -475,37 +505,48 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           const uint32_t key = keys[i][j];
           const bool act = key != kKeyNegInf && (p == 0 || (key >> hshift) == prefix);
           hist_add(h, act, (key >> shift) & dmask);
-          kmin = act && key < kmin ? key : kmin;
-          kmax = act && key > kmax ? key : kmax;
+          if (track) {
+            kmin = act && key < kmin ? key : kmin;
+            kmax = act && key > kmax ? key : kmax;
+          }
         }
       }
     }
-    kmin = wave_reduce_minmax<true>(kmin);
-    kmax = wave_reduce_minmax<false>(kmax);
-    if (lane == 0) {
-      sm.wmin[w] = kmin;
-      sm.wmax[w] = kmax;
+    if (track) {
+      kmin = wave_reduce_minmax<true>(kmin);
+      kmax = wave_reduce_minmax<false>(kmax);
+      if (lane == 0) {
+        sm.wmin[w] = kmin;
+        sm.wmax[w] = kmax;
+      }
     }
     __syncthreads();
     // Wave 0 alone finds the bin: lane l owns the 32 bins [kBins - 32(l+1),
-    // kBins - 32l), read from the top down, and one wave scan of the lanes'
-    // totals gives the counts above each lane. It also reduces the per-wave
-    // key ranges. The other waves clear the next pass's histogram meanwhile.
+    // kBins - 32l), and one wave scan of the lanes' totals gives the counts
+    // above each lane. The totals are read in a lane-rotated chunk order: the
+    // lanes' runs are 128 bytes apart, so in-order reads would all start on one
+    // bank. The lane that holds the need-th key then walks its own chunks from
+    // the top down. Where a pass has a key range (above), wave 0 also reduces
+    // the per-wave ranges. The other waves clear the next pass's histogram
+    // meanwhile.
     if (w == 0) {
       const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
-      uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 v = hv[7 - j];
-        g8[j] = v.x + v.y + v.z + v.w;
-      }
       uint32_t loc = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) loc += g8[j];
+      for (int j = 0; j < 8; ++j) {
+        const uint4 v = hv[(j + lane) & 7];
+        loc += v.x + v.y + v.z + v.w;
+      }
       const uint32_t incl = wave_incl_scan(loc);
       if (p == 0 && lane == kWave - 1) sm.n_cand = incl;
       uint32_t cum = incl - loc;
       if (cum < need && need <= incl) {  // one lane: the need-th key is in its bins
+        uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 v = hv[7 - j];
+          g8[j] = v.x + v.y + v.z + v.w;
+        }
         int jj = 0;
         uint32_t before = cum;
 #pragma unroll
@@ -529,12 +570,14 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           cum += c4[k];
         }
       }
-      uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
-      uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
-      lo = wave_reduce_minmax<true>(lo);
-      hi = wave_reduce_minmax<false>(hi);
-      if (lane == 0) sm.all_same = lo == hi ? 1u : 0u;
-      if (lane == 0) sm.same_key = lo;
+      if (p == 0 || (!BLOCKED && p == 1)) {
+        uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
+        uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
+        lo = wave_reduce_minmax<true>(lo);
+        hi = wave_reduce_minmax<false>(hi);
+        if (lane == 0) sm.all_same = lo == hi ? 1u : 0u;
+        if (lane == 0) sm.same_key = lo;
+      }
     } else {
       for (int i = t - kWave; i < kBins; i += NT - kWave) sm.hist[buf ^ 1][i] = 0u;
     }
@@ -546,9 +589,9 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         break;
       }
     }
-    // every active key is the same value: the threshold is that key, of which
+    // every key in play is the same value: the threshold is that key, of which
     // `need` are taken (identical keys would only fill one bin per later pass)
-    if (sm.all_same) {
+    if ((p == 0 || (!BLOCKED && p == 1)) && sm.all_same) {
       prefix = sm.same_key;
       level = kPasses;
       break;
@@ -587,8 +630,10 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     const uint32_t incl = wave_incl_scan(packed);
     if (lane == kWave - 1) sm.wpack[w] = incl;
     __syncthreads();
-    uint32_t before = incl - packed;
-    for (int ww = 0; ww < w; ++ww) before += sm.wpack[ww];
+    // counts of the waves before this one: a scan over the per-wave totals
+    const uint32_t wscan = wave_incl_scan(lane < NW ? sm.wpack[lane] : 0u);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t before = incl - packed + (wu > 0 ? readlane<uint32_t>(wscan, wu - 1) : 0u);
     uint32_t gb = before & 0xFFFFu, eb = before >> 16;
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
@@ -695,10 +740,6 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       // ids to order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
       sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, out);
     }
-  }
-  if (stage_zero != nullptr) {
-    if (!cached) __syncthreads();  // streamed rows: every read of the row is done
-    for (int i = t; i < n; i += NT) stage_zero[i] = 0.f;
   }
 }
 

@@ -33,10 +33,11 @@
  *     per argument). Integer arrays must be 4-byte aligned.
  *   - bf16 data is passed as raw 16-bit patterns (uint16_t storage).
  *   - Workspace: a caller-owned device buffer of at least the size the
- *     matching *_workspace_bytes() returns. An idx_select workspace must be
- *     zero-filled once before its first use (every call returns it to zero). One workspace may serve any sequence of calls on
- *     one stream; calls that may overlap (other streams) need distinct
- *     workspaces.
+ *     matching *_workspace_bytes() returns. A workspace must be zero-filled
+ *     once before its first use: it holds arrival counters, which every call
+ *     returns to zero, and scratch, which calls overwrite before reading. One
+ *     workspace may serve any sequence of calls on one stream; calls that may
+ *     overlap (other streams) need distinct workspaces.
  */
 #ifndef IDX_H
 #define IDX_H
@@ -114,8 +115,9 @@ int idx_score(const void* q, const void* c, const int32_t* seq_len, float* score
  * few and long: each row is then cut into segments selected by several
  * workgroups and merged by the last to finish (arrival counters and segment
  * candidates live in the workspace). It must be zero-filled before first use;
- * every call returns it to that state, so it may serve any later call that
- * fits it. Calls that may overlap (other streams) need distinct workspaces.
+ * every call returns its arrival counters to zero (the candidates are scratch),
+ * so it may serve any later call that fits it. Calls that may overlap (other
+ * streams) need distinct workspaces.
  */
 size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags);
 int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
@@ -133,8 +135,9 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
  * B <= IDX_MAX_REQUESTS.
  * ws / ws_bytes: workspace of at least idx_workspace_bytes(B, N_pad, H, K, flags)
  * bytes, zero-filled before first use: 2 MiB of per-request arrival counters
- * (one 128-byte line each) and staging for the scores. Every call returns the whole workspace to zero,
- * so one workspace may serve calls of any shape that fits it.
+ * (one 128-byte line each), which every call returns to zero, and staging for
+ * the scores (scratch), so one workspace may serve calls of any shape that fits
+ * it.
  */
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags);
 int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
