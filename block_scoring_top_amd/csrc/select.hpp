@@ -51,6 +51,7 @@ struct SelectSmem {
   uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
   uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the row's active keys
   uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
+  uint32_t n_gather, gather[kWave];  // the keys of a small threshold bin
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
 };
@@ -416,6 +417,60 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
   }
 }
 
+// Wave 0 (all 64 lanes) finds the bin of h that holds the need-th largest of
+// the counted keys, bins ranked from the top (kBins - 1) down: sm.sel_bin,
+// sm.sel_need (need minus the keys in higher bins) and sm.sel_tot (the bin's
+// count); with `total`, sm.n_cand gets the histogram's total. Lane l owns the
+// 32 bins [kBins - 32(l+1), kBins - 32l), and one wave scan of the lanes'
+// totals gives the counts above each lane. The totals are read in a
+// lane-rotated chunk order: the lanes' runs are 128 bytes apart, so in-order
+// reads would all start on one bank. The lane that holds the need-th key then
+// walks its own chunks from the top down.
+template <class SM>
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, bool total, SM& sm) {
+  const int lane = lane_id();
+  const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
+  uint32_t loc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 v = hv[(j + lane) & 7];
+    loc += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t incl = wave_incl_scan(loc);
+  if (total && lane == kWave - 1) sm.n_cand = incl;
+  uint32_t cum = incl - loc;
+  if (cum < need && need <= incl) {  // one lane: the need-th key is in its bins
+    uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = hv[7 - j];
+      g8[j] = v.x + v.y + v.z + v.w;
+    }
+    int jj = 0;
+    uint32_t before = cum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (cum < need && need <= cum + g8[j]) {
+        jj = j;
+        before = cum;
+      }
+      cum += g8[j];
+    }
+    const uint4 v = hv[7 - jj];
+    const uint32_t c4[4] = {v.w, v.z, v.y, v.x};
+    cum = before;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (cum < need && need <= cum + c4[k]) {
+        sm.sel_bin = (uint32_t)(kBins - 1 - 32 * lane - 4 * jj - k);
+        sm.sel_need = need - cum;
+        sm.sel_tot = c4[k];
+      }
+      cum += c4[k];
+    }
+  }
+}
+
 // BLOCKED: the caller guarantees n <= NT * SLOTS * 4; the row is held in the
 // blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
 // when it does not fit one register tile).
@@ -478,14 +533,113 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
   __syncthreads();
 
-  // Each pass histograms the next digit of the keys that still match the
-  // resolved prefix, then finds the bin holding the need-th largest of them:
-  // wave 0 scans the bins from the top (see below).
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
   int level = 0;  // digits resolved (kPasses = the whole key)
-  bool take_all = false;
-  for (int p = 0; p < kPasses; ++p) {
-    const int buf = p & 1;
+  bool take_all = false, resolved = false;
+  int boff = 0;  // histogram buffer of the first radix pass
+
+  // Blocked rows first try one pass over linear value bins: with the row's
+  // range [lo, hi], key x goes to bin floor((x - lo) * kBins / (hi - lo)),
+  // clamped to the last bin (monotone in x, so a higher bin never holds a
+  // smaller key). On spread-out scores the bin of the K-th key then holds a
+  // few keys, where the first 11-bit digit (sign, exponent, two mantissa bits)
+  // leaves tens to hundreds, and a second radix pass would follow. When that
+  // bin holds at most 64 keys, they are gathered in LDS and wave 0 ranks them:
+  // the threshold is then an exact key. Otherwise (ranges that are not finite,
+  // clustered or tied rows) the radix passes below resolve the row.
+  if constexpr (BLOCKED) {
+    uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
+    uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
+    lo = wave_reduce_minmax<true>(lo);
+    hi = wave_reduce_minmax<false>(hi);
+    const float flo = key_to_score(lo), fhi = key_to_score(hi);
+    const float span = fhi - flo;
+    const float scale = (float)kBins / span;
+    // the same values in every wave: the branch is uniform over the workgroup
+    if (lo < hi && __builtin_isfinite(flo) && __builtin_isfinite(fhi) &&
+        __builtin_isfinite(span) && span > 0.f && __builtin_isfinite(scale)) {
+      const float off = -flo * scale;
+      uint32_t* h = sm.hist[0];
+      uint32_t bins[SLOTS][4];
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t key = keys[i][j];
+          const float x = __builtin_fmaf(key_to_score(key), scale, off);
+          const uint32_t bin = x > 0.f ? min((uint32_t)kBins - 1u, (uint32_t)fminf(x, 4096.f)) : 0u;
+          bins[i][j] = bin;
+          hist_add(h, key != kKeyNegInf, bin);
+        }
+      }
+      __syncthreads();
+      if (w == 0) {
+        find_bin(h, need, true, sm);
+        if (lane == 0) sm.n_gather = 0u;
+      } else {
+        for (int i = t - kWave; i < kBins; i += NT - kWave) sm.hist[1][i] = 0u;
+      }
+      __syncthreads();
+      ncand = sm.n_cand;
+      const uint32_t sb = sm.sel_bin, bneed = sm.sel_need, btot = sm.sel_tot;
+      if (ncand <= (uint32_t)K) {
+        take_all = true;
+        resolved = true;
+      } else if (btot <= (uint32_t)kWave) {
+        // gather the bin's keys: one slot reservation per wave and key slot
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+          if (!slot_live(0, i)) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool g = keys[i][j] != kKeyNegInf && bins[i][j] == sb;
+            const uint64_t gm = ballot(g);
+            if (gm != 0) {
+              const int l0 = __builtin_ctzll(gm);
+              uint32_t base = 0;
+              if (lane == l0) base = atomicAdd(&sm.n_gather, popc64(gm));
+              base = readlane<uint32_t>(base, l0);
+              if (g) sm.gather[base + mbcnt(gm)] = keys[i][j];
+            }
+          }
+        }
+        __syncthreads();
+        if (w == 0) {
+          // lane l ranks gathered key c: gt keys above it, eq equal to it; the
+          // threshold is the key with gt < bneed <= gt + eq
+          const uint32_t c = (uint32_t)lane < btot ? sm.gather[lane] : 0u;
+          uint32_t gt = 0, eq = 0;
+          for (uint32_t j = 0; j < btot; ++j) {
+            const uint32_t x = readlane<uint32_t>(c, (int)j);
+            gt += x > c ? 1u : 0u;
+            eq += x == c ? 1u : 0u;
+          }
+          const uint64_t hm = ballot((uint32_t)lane < btot && gt < bneed && bneed <= gt + eq);
+          const int l0 = hm != 0 ? __builtin_ctzll(hm) : 0;  // hm != 0: 1 <= bneed <= btot
+          const uint32_t tkey = readlane<uint32_t>(c, l0);
+          const uint32_t tgt = readlane<uint32_t>(gt, l0);
+          if (lane == 0) {
+            sm.same_key = tkey;
+            sm.sel_need = bneed - tgt;
+          }
+        }
+        __syncthreads();
+        prefix = sm.same_key;
+        need = sm.sel_need;
+        level = kPasses;
+        resolved = true;
+      } else {
+        boff = 1;  // histogram 0 holds the linear counts; histogram 1 is clear
+      }
+    }
+  }
+
+  // Each pass histograms the next digit of the keys that still match the
+  // resolved prefix, then finds the bin holding the need-th largest of them
+  // (wave 0, find_bin above).
+  for (int p = 0; p < (resolved ? 0 : kPasses); ++p) {
+    const int buf = (p + boff) & 1;
     uint32_t* h = sm.hist[buf];
     const int shift = digit_shift(p);
     const uint32_t dmask = digit_mask(p);
@@ -521,55 +675,11 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       }
     }
     __syncthreads();
-    // Wave 0 alone finds the bin: lane l owns the 32 bins [kBins - 32(l+1),
-    // kBins - 32l), and one wave scan of the lanes' totals gives the counts
-    // above each lane. The totals are read in a lane-rotated chunk order: the
-    // lanes' runs are 128 bytes apart, so in-order reads would all start on one
-    // bank. The lane that holds the need-th key then walks its own chunks from
-    // the top down. Where a pass has a key range (above), wave 0 also reduces
-    // the per-wave ranges. The other waves clear the next pass's histogram
-    // meanwhile.
+    // Wave 0 finds the bin, and where a pass has a key range (above) also
+    // reduces the per-wave ranges; the other waves clear the next pass's
+    // histogram meanwhile.
     if (w == 0) {
-      const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
-      uint32_t loc = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 v = hv[(j + lane) & 7];
-        loc += v.x + v.y + v.z + v.w;
-      }
-      const uint32_t incl = wave_incl_scan(loc);
-      if (p == 0 && lane == kWave - 1) sm.n_cand = incl;
-      uint32_t cum = incl - loc;
-      if (cum < need && need <= incl) {  // one lane: the need-th key is in its bins
-        uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint4 v = hv[7 - j];
-          g8[j] = v.x + v.y + v.z + v.w;
-        }
-        int jj = 0;
-        uint32_t before = cum;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (cum < need && need <= cum + g8[j]) {
-            jj = j;
-            before = cum;
-          }
-          cum += g8[j];
-        }
-        const uint4 v = hv[7 - jj];
-        const uint32_t c4[4] = {v.w, v.z, v.y, v.x};
-        cum = before;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (cum < need && need <= cum + c4[k]) {
-            sm.sel_bin = (uint32_t)(kBins - 1 - 32 * lane - 4 * jj - k);
-            sm.sel_need = need - cum;
-            sm.sel_tot = c4[k];
-          }
-          cum += c4[k];
-        }
-      }
+      find_bin(h, need, p == 0, sm);
       if (p == 0 || (!BLOCKED && p == 1)) {
         uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
         uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
