@@ -167,12 +167,21 @@ __device__ __forceinline__ void load_keys_blocked(const float* row, int n, int c
       }
     }
   }
+  if (e_base + kpt4 <= n) {  // every entry of the thread is in the row (all but the last threads)
 #pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
+    for (int i = 0; i < SLOTS; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e_base + 4 * i + j;
-      keys[i][j] = (4 * i < kpt4 && e < n) ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+      for (int j = 0; j < 4; ++j)
+        keys[i][j] = 4 * i < kpt4 ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e_base + 4 * i + j;
+        keys[i][j] = (4 * i < kpt4 && e < n) ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+      }
     }
   }
 }
@@ -568,9 +577,22 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         for (int j = 0; j < 4; ++j) {
           const uint32_t key = keys[i][j];
           const float x = __builtin_fmaf(key_to_score(key), scale, off);
-          const uint32_t bin = x > 0.f ? min((uint32_t)kBins - 1u, (uint32_t)fminf(x, 4096.f)) : 0u;
+          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1));
           bins[i][j] = bin;
-          hist_add(h, key != kKeyNegInf, bin);
+          // Spread-out bins rarely collide within a wave, so lanes add their
+          // own counts; a wave whose active lanes all share one bin (clustered
+          // rows; active lanes are a prefix of the wave, so lane 0 is one of
+          // them) adds them with one atomic instead of 64 serialised ones.
+          const bool act = key != kKeyNegInf;
+          const uint64_t m = ballot(act);
+          if (m != 0) {
+            const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
+            if ((ballot(bin == b0) & m) == m) {
+              if (lane == 0) atomicAdd(&h[b0], popc64(m));
+            } else if (act) {
+              atomicAdd(&h[bin], 1u);
+            }
+          }
         }
       }
       __syncthreads();
@@ -713,30 +735,32 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   }
 
   // ---- emit --------------------------------------------------------------------------
-  const int shiftL = take_all ? 0 : (level == 1 ? 21 : (level == 2 ? 10 : 0));
+  // The taken keys as two key bounds: a key above hi_b is taken; a key in
+  // [lo_b, hi_b] is a threshold copy, of which the first need_e in index order
+  // are taken. Every scored key is above kKeyNegInf (NaN scores are outside the
+  // contract), so with take_all (lo_b = hi_b = kKeyNegInf, need_e = 0) every
+  // scored key is taken and only unscored entries fall in the threshold range.
+  const int shiftL = level == 1 ? kDigit0Shift : (level == 2 ? 10 : 0);
+  const uint32_t lo_b = take_all ? kKeyNegInf : prefix << shiftL;
+  const uint32_t hi_b = take_all ? kKeyNegInf : lo_b | ((1u << shiftL) - 1u);
+  const uint32_t need_e = take_all ? 0u : need;
   const uint32_t m_out = take_all ? ncand : (uint32_t)K;
-  auto classify = [&](uint32_t key, bool& gt, bool& eq) {
-    const bool act = key != kKeyNegInf;
-    const uint32_t hi = take_all ? 0u : (key >> shiftL);
-    gt = act && (take_all || hi > prefix);
-    eq = act && !take_all && hi == prefix;
-  };
   if constexpr (BLOCKED) {
     // Blocked layout: each thread counts its taken-for-sure (gt) and threshold
     // (eq) keys, one workgroup scan of the packed counts (eq << 16 | gt; both
     // fit 16 bits since n <= 32768) gives the keys before the thread, and the
     // thread then writes its taken ids in ascending order.
-    uint32_t packed = 0;
+    uint32_t ngt = 0, nge = 0;
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       if (!slot_live(0, i)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bool gt, eq;
-        classify(keys[i][j], gt, eq);
-        packed += (gt ? 1u : 0u) + (eq ? 0x10000u : 0u);
+        ngt += keys[i][j] > hi_b ? 1u : 0u;
+        nge += keys[i][j] >= lo_b ? 1u : 0u;
       }
     }
+    const uint32_t packed = ngt + ((nge - ngt) << 16);
     const uint32_t incl = wave_incl_scan(packed);
     if (lane == kWave - 1) sm.wpack[w] = incl;
     __syncthreads();
@@ -750,10 +774,10 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       if (!slot_live(0, i)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bool gt, eq;
-        classify(keys[i][j], gt, eq);
-        const bool take = gt || (eq && eb < need);
-        const uint32_t pos = gb + (eb < need ? eb : need);
+        const bool gt = keys[i][j] > hi_b;
+        const bool eq = !gt && keys[i][j] >= lo_b;
+        const bool take = gt || (eq && eb < need_e);
+        const uint32_t pos = gb + min(eb, need_e);
         if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
           const int id = t * kpt4 + 4 * i + j;
           if constexpr (SORTED) {
@@ -780,12 +804,9 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t key = keys[i][j];
-          const bool act = key != kKeyNegInf;
-          const uint32_t hi = take_all ? 0u : (key >> shiftL);
-          const bool gt = act && (take_all || hi > prefix);
-          const bool eq = act && !take_all && hi == prefix;
+          const bool gt = key > hi_b;
           g += popc64(ballot(gt));
-          e += popc64(ballot(eq));
+          e += popc64(ballot(!gt && key >= lo_b));
         }
       }
       if (lane == 0) {
@@ -806,17 +827,15 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t key = keys[i][j];
-        const bool act = key != kKeyNegInf;
-        const uint32_t hi = take_all ? 0u : (key >> shiftL);
-        gt[j] = act && (take_all || hi > prefix);
-        eq[j] = act && !take_all && hi == prefix;
+        gt[j] = key > hi_b;
+        eq[j] = !gt[j] && key >= lo_b;
         gb += mbcnt(ballot(gt[j]));
         eb += mbcnt(ballot(eq[j]));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool take = gt[j] || (eq[j] && eb < need);
-        const uint32_t pos = gb + (eb < need ? eb : need);
+        const bool take = gt[j] || (eq[j] && eb < need_e);
+        const uint32_t pos = gb + min(eb, need_e);
         if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
           const int id = tbase + (i * NT + t) * 4 + j;
           if constexpr (SORTED) {
