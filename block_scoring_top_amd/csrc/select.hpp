@@ -52,6 +52,7 @@ struct SelectSmem {
   uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the row's active keys
   uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
   uint32_t n_gather, gather[kWave];  // the keys of a small threshold bin
+  uint32_t wtot[NW];                 // per-wave bin totals of the bin search
   uint32_t cgt[E], ceq[E];
   uint32_t tot_gt, tot_eq;
 };
@@ -426,56 +427,60 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
   }
 }
 
-// Wave 0 (all 64 lanes) finds the bin of h that holds the need-th largest of
-// the counted keys, bins ranked from the top (kBins - 1) down: sm.sel_bin,
-// sm.sel_need (need minus the keys in higher bins) and sm.sel_tot (the bin's
-// count); with `total`, sm.n_cand gets the histogram's total. Lane l owns the
-// 32 bins [kBins - 32(l+1), kBins - 32l), and one wave scan of the lanes'
-// totals gives the counts above each lane. The totals are read in a
-// lane-rotated chunk order: the lanes' runs are 128 bytes apart, so in-order
-// reads would all start on one bank. The lane that holds the need-th key then
-// walks its own chunks from the top down.
-template <class SM>
-__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, bool total, SM& sm) {
+// All NW waves find the bin of h that holds the need-th largest of the counted
+// keys, bins ranked from the top (kBins - 1) down: sm.sel_bin, sm.sel_need
+// (need minus the keys in higher bins), sm.sel_tot (the bin's count) and
+// sm.n_cand (the histogram's total). Wave w covers the kBins / NW bins below
+// kBins - w * kBins / NW, each lane a run of BPL consecutive bins read as one
+// vector (consecutive lanes, consecutive runs: no bank conflicts); a wave scan
+// gives the counts above each lane within the wave, and after one barrier a
+// scan of the per-wave totals gives the counts above each wave. The lane whose
+// run holds the need-th key then walks its bins. Ends with a barrier; the
+// results are read after the caller's next barrier. `clear` (may be null),
+// kBins words, is zeroed on the way.
+template <int NT, class SM>
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, SM& sm,
+                                         uint32_t* clear) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPL = kBins / NT;  // bins per lane: 2, 4 or 8
+  static_assert(BPL == 2 || BPL == 4 || BPL == 8, "2048 bins over 256..1024 threads");
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const uint4* hv = reinterpret_cast<const uint4*>(h + kBins - 32 * (lane + 1));
+  const int top = kBins - (w * kWave + lane) * BPL;  // this lane's bins: [top - BPL, top)
+  uint32_t c[BPL];  // c[k] = h[top - 1 - k]: descending
+  if constexpr (BPL == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(h + top - 2);
+    c[0] = v.y; c[1] = v.x;
+  } else {
+#pragma unroll
+    for (int r = 0; r < BPL / 4; ++r) {
+      const uint4 v = *reinterpret_cast<const uint4*>(h + top - 4 * (r + 1));
+      c[4 * r] = v.w; c[4 * r + 1] = v.z; c[4 * r + 2] = v.y; c[4 * r + 3] = v.x;
+    }
+  }
   uint32_t loc = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint4 v = hv[(j + lane) & 7];
-    loc += v.x + v.y + v.z + v.w;
-  }
+  for (int k = 0; k < BPL; ++k) loc += c[k];
   const uint32_t incl = wave_incl_scan(loc);
-  if (total && lane == kWave - 1) sm.n_cand = incl;
-  uint32_t cum = incl - loc;
-  if (cum < need && need <= incl) {  // one lane: the need-th key is in its bins
-    uint32_t g8[8];  // g8[j]: the 4 bins of hv[7 - j] (bins in descending order)
+  if (lane == kWave - 1) sm.wtot[w] = incl;
+  if (clear != nullptr) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 v = hv[7 - j];
-      g8[j] = v.x + v.y + v.z + v.w;
-    }
-    int jj = 0;
-    uint32_t before = cum;
+    for (int k = 0; k < BPL; ++k) clear[threadIdx.x * BPL + k] = 0u;
+  }
+  __syncthreads();
+  const uint32_t ws = wave_incl_scan(lane < NW ? sm.wtot[lane] : 0u);
+  const uint32_t above = w > 0 ? readlane<uint32_t>(ws, w - 1) : 0u;
+  if (w == 0 && lane == 0) sm.n_cand = readlane<uint32_t>(ws, NW - 1);
+  uint32_t cum = above + incl - loc;
+  if (cum < need && need <= cum + loc) {  // one lane: the need-th key is in its bins
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (cum < need && need <= cum + g8[j]) {
-        jj = j;
-        before = cum;
-      }
-      cum += g8[j];
-    }
-    const uint4 v = hv[7 - jj];
-    const uint32_t c4[4] = {v.w, v.z, v.y, v.x};
-    cum = before;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (cum < need && need <= cum + c4[k]) {
-        sm.sel_bin = (uint32_t)(kBins - 1 - 32 * lane - 4 * jj - k);
+    for (int k = 0; k < BPL; ++k) {
+      if (cum < need && need <= cum + c[k]) {
+        sm.sel_bin = (uint32_t)(top - 1 - k);
         sm.sel_need = need - cum;
-        sm.sel_tot = c4[k];
+        sm.sel_tot = c[k];
       }
-      cum += c4[k];
+      cum += c[k];
     }
   }
 }
@@ -595,18 +600,32 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           }
         }
       }
-      __syncthreads();
-      if (w == 0) {
-        find_bin(h, need, true, sm);
-        if (lane == 0) sm.n_gather = 0u;
-      } else {
-        for (int i = t - kWave; i < kBins; i += NT - kWave) sm.hist[1][i] = 0u;
+      if (t == 0) {
+        sm.n_gather = 0u;
+        sm.same_key = 0xFFFFFFFFu;
       }
+      __syncthreads();
+      find_bin<NT>(h, need, sm, sm.hist[1]);
       __syncthreads();
       ncand = sm.n_cand;
       const uint32_t sb = sm.sel_bin, bneed = sm.sel_need, btot = sm.sel_tot;
       if (ncand <= (uint32_t)K) {
         take_all = true;
+        resolved = true;
+      } else if (btot == bneed) {
+        // the bin is taken whole: the threshold is its smallest key, and every
+        // copy of that key is taken (all keys at or above it make K)
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+          if (!slot_live(0, i)) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (keys[i][j] != kKeyNegInf && bins[i][j] == sb) atomicMin(&sm.same_key, keys[i][j]);
+        }
+        __syncthreads();
+        prefix = sm.same_key;
+        need = 0xFFFFFFFFu;
+        level = kPasses;
         resolved = true;
       } else if (btot <= (uint32_t)kWave) {
         // gather the bin's keys: one slot reservation per wave and key slot
@@ -697,11 +716,10 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       }
     }
     __syncthreads();
-    // Wave 0 finds the bin, and where a pass has a key range (above) also
-    // reduces the per-wave ranges; the other waves clear the next pass's
-    // histogram meanwhile.
+    // All waves find the bin and clear the next pass's histogram; where a pass
+    // has a key range (above), wave 0 also reduces the per-wave ranges.
+    find_bin<NT>(h, need, sm, sm.hist[buf ^ 1]);
     if (w == 0) {
-      find_bin(h, need, p == 0, sm);
       if (p == 0 || (!BLOCKED && p == 1)) {
         uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
         uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
@@ -710,8 +728,6 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         if (lane == 0) sm.all_same = lo == hi ? 1u : 0u;
         if (lane == 0) sm.same_key = lo;
       }
-    } else {
-      for (int i = t - kWave; i < kBins; i += NT - kWave) sm.hist[buf ^ 1][i] = 0u;
     }
     __syncthreads();
     if (p == 0) {
