@@ -367,6 +367,7 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int P, uint64_t* 
 //
 // IdsOut: the ids themselves, -1 in unused slots.
 struct IdsOut {
+  static constexpr bool kUsesKey = false;  // put() ignores its key argument
   int32_t* ids;
   __device__ __forceinline__ void put(int pos, int id, uint32_t) const { ids[pos] = id; }
   __device__ __forceinline__ void pad(int k) const { ids[k] = -1; }
@@ -381,6 +382,7 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
 // written with agent-scope stores for the workgroup that merges the segments;
 // unused slots hold -inf (never selected).
 struct CandOut {
+  static constexpr bool kUsesKey = true;  // the score is written beside the id
   float* score;
   int32_t* id;
   int base;  // the segment's first index in the row
@@ -397,6 +399,7 @@ struct CandOut {
 // MappedIdsOut: selecting over a candidate list, the id of candidate i is
 // map[i] (written by other workgroups: read with agent-scope loads).
 struct MappedIdsOut {
+  static constexpr bool kUsesKey = false;
   int32_t* ids;
   const int32_t* map;
   __device__ __forceinline__ void put(int pos, int i, uint32_t) const {
@@ -550,6 +553,10 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
   int level = 0;  // digits resolved (kPasses = the whole key)
   bool take_all = false, resolved = false;
+  // simple threshold: exactly the keys whose class value (the key, or below
+  // the linear bin) is at least t_lo are taken, with no partial tie
+  bool simple = false;
+  uint32_t t_lo = 0u;
   int boff = 0;  // histogram buffer of the first radix pass
 
   // Blocked rows first try one pass over linear value bins: with the row's
@@ -612,9 +619,20 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       if (ncand <= (uint32_t)K) {
         take_all = true;
         resolved = true;
+      } else if (btot == bneed && !SORTED && !Out::kUsesKey && sb > 0) {
+        // the bin is taken whole and only ids are written: the keys of bins
+        // sb and above are taken, so the bins become the class values (scored
+        // keys below the bin, and unscored ones in bin 0, stay below sb)
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) keys[i][j] = bins[i][j];
+        simple = true;
+        t_lo = sb;
+        resolved = true;
       } else if (btot == bneed) {
         // the bin is taken whole: the threshold is its smallest key, and every
-        // copy of that key is taken (all keys at or above it make K)
+        // key at or above it is taken (they make K)
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
           if (!slot_live(0, i)) continue;
@@ -623,9 +641,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
             if (keys[i][j] != kKeyNegInf && bins[i][j] == sb) atomicMin(&sm.same_key, keys[i][j]);
         }
         __syncthreads();
-        prefix = sm.same_key;
-        need = 0xFFFFFFFFu;
-        level = kPasses;
+        simple = true;
+        t_lo = sm.same_key;
         resolved = true;
       } else if (btot <= (uint32_t)kWave) {
         // gather the bin's keys: one slot reservation per wave and key slot
@@ -747,63 +764,103 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     prefix = (prefix << (p == 2 ? 10 : 11)) | sm.sel_bin;
     need = sm.sel_need;
     level = p + 1;
-    if (sm.sel_tot == need) break;  // the whole bin is taken: nothing left to resolve
+    if (sm.sel_tot == need) {  // the whole bin is taken: every key from its lowest on
+      simple = true;
+      t_lo = prefix << digit_shift(p);
+      break;
+    }
   }
 
   // ---- emit --------------------------------------------------------------------------
-  // The taken keys as two key bounds: a key above hi_b is taken; a key in
+  // The taken keys as two class bounds: a key above hi_b is taken; a key in
   // [lo_b, hi_b] is a threshold copy, of which the first need_e in index order
-  // are taken. Every scored key is above kKeyNegInf (NaN scores are outside the
-  // contract), so with take_all (lo_b = hi_b = kKeyNegInf, need_e = 0) every
-  // scored key is taken and only unscored entries fall in the threshold range.
+  // are taken. A simple threshold t_lo is hi_b = t_lo - 1 with an empty copy
+  // range. Every scored key is above kKeyNegInf (NaN scores are outside the
+  // contract), so take_all is the simple threshold kKeyNegInf + 1.
+  if (take_all) {
+    simple = true;
+    t_lo = kKeyNegInf + 1u;
+  }
   const int shiftL = level == 1 ? kDigit0Shift : (level == 2 ? 10 : 0);
-  const uint32_t lo_b = take_all ? kKeyNegInf : prefix << shiftL;
-  const uint32_t hi_b = take_all ? kKeyNegInf : lo_b | ((1u << shiftL) - 1u);
-  const uint32_t need_e = take_all ? 0u : need;
+  const uint32_t lo_b = simple ? t_lo : prefix << shiftL;
+  const uint32_t hi_b = simple ? t_lo - 1u : lo_b | ((1u << shiftL) - 1u);
+  const uint32_t need_e = simple ? 0u : need;
   const uint32_t m_out = take_all ? ncand : (uint32_t)K;
   if constexpr (BLOCKED) {
     // Blocked layout: each thread counts its taken-for-sure (gt) and threshold
-    // (eq) keys, one workgroup scan of the packed counts (eq << 16 | gt; both
-    // fit 16 bits since n <= 32768) gives the keys before the thread, and the
-    // thread then writes its taken ids in ascending order.
-    uint32_t ngt = 0, nge = 0;
+    // (eq) keys, one workgroup scan of the counts gives the keys before the
+    // thread, and the thread then writes its taken ids in ascending order.
+    auto count_before = [&](uint32_t mine) {  // workgroup exclusive scan
+      const uint32_t incl = wave_incl_scan(mine);
+      if (lane == kWave - 1) sm.wpack[w] = incl;
+      __syncthreads();
+      // counts of the waves before this one: a scan over the per-wave totals
+      const uint32_t wscan = wave_incl_scan(lane < NW ? sm.wpack[lane] : 0u);
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      return incl - mine + (wu > 0 ? readlane<uint32_t>(wscan, wu - 1) : 0u);
+    };
+    if (simple) {
+      uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      if (!slot_live(0, i)) continue;
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ngt += keys[i][j] > hi_b ? 1u : 0u;
-        nge += keys[i][j] >= lo_b ? 1u : 0u;
+        for (int j = 0; j < 4; ++j) cnt += keys[i][j] >= t_lo ? 1u : 0u;
       }
-    }
-    const uint32_t packed = ngt + ((nge - ngt) << 16);
-    const uint32_t incl = wave_incl_scan(packed);
-    if (lane == kWave - 1) sm.wpack[w] = incl;
-    __syncthreads();
-    // counts of the waves before this one: a scan over the per-wave totals
-    const uint32_t wscan = wave_incl_scan(lane < NW ? sm.wpack[lane] : 0u);
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    const uint32_t before = incl - packed + (wu > 0 ? readlane<uint32_t>(wscan, wu - 1) : 0u);
-    uint32_t gb = before & 0xFFFFu, eb = before >> 16;
+      uint32_t g = count_before(cnt);
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      if (!slot_live(0, i)) continue;
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool gt = keys[i][j] > hi_b;
-        const bool eq = !gt && keys[i][j] >= lo_b;
-        const bool take = gt || (eq && eb < need_e);
-        const uint32_t pos = gb + min(eb, need_e);
-        if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
-          const int id = t * kpt4 + 4 * i + j;
-          if constexpr (SORTED) {
-            sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
-          } else {
-            out.put((int)pos, id, keys[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          const bool take = keys[i][j] >= t_lo;
+          if (take && g < m_out) {  // g < m_out always holds; the test only bounds the store
+            const int id = t * kpt4 + 4 * i + j;
+            if constexpr (SORTED) {
+              sortbuf[g] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
+            } else {
+              out.put((int)g, id, keys[i][j]);
+            }
           }
+          g += take ? 1u : 0u;
         }
-        gb += gt ? 1u : 0u;
-        eb += eq ? 1u : 0u;
+      }
+    } else {
+      // threshold copies: packed counts (eq << 16 | gt; both fit 16 bits since
+      // n <= 32768)
+      uint32_t ngt = 0, nge = 0;
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ngt += keys[i][j] > hi_b ? 1u : 0u;
+          nge += keys[i][j] >= lo_b ? 1u : 0u;
+        }
+      }
+      const uint32_t packed = ngt + ((nge - ngt) << 16);
+      const uint32_t before = count_before(packed);
+      uint32_t gb = before & 0xFFFFu, eb = before >> 16;
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool gt = keys[i][j] > hi_b;
+          const bool eq = !gt && keys[i][j] >= lo_b;
+          const bool take = gt || (eq && eb < need_e);
+          const uint32_t pos = gb + min(eb, need_e);
+          if (take && pos < m_out) {  // pos < m_out always holds; the test only bounds the store
+            const int id = t * kpt4 + 4 * i + j;
+            if constexpr (SORTED) {
+              sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
+            } else {
+              out.put((int)pos, id, keys[i][j]);
+            }
+          }
+          gb += gt ? 1u : 0u;
+          eb += eq ? 1u : 0u;
+        }
       }
     }
   }
