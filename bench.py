@@ -559,7 +559,7 @@ def parse_pmc(dirs, out_path, workload):
         for ctr, d in zip(("FETCH_SIZE", "WRITE_SIZE"), dirs):
             f.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d /root/repo/{d} -o pmc -- "
                     f"python3 /root/repo/bench.py --workload {workload} --steps 20 --warmup 5 "
-                    "--no-cpu-baseline --no-graph --pmc-calibrate\n")
+                    "--no-cpu-baseline --no-graph --no-extras --pmc-calibrate\n")
         f.write(f"#   python3 bench.py --workload {workload} --parse-pmc {' '.join(dirs)}\n")
         for k_, v in res.items():
             f.write(f"{k_}={v}\n")

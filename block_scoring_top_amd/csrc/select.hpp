@@ -131,7 +131,8 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int cap, int 
 // or past n become kKeyNegInf. Loads are issued before any is used.
 template <int NT, int SLOTS, bool COHERENT>
 __device__ __forceinline__ void load_keys_blocked(const float* row, int n, int cap, int kpt4,
-                                                  uint32_t (&keys)[SLOTS][4]) {
+                                                  uint32_t (&keys)[SLOTS][4],
+                                                  uint32_t (&raw)[SLOTS][4]) {
   const int t = threadIdx.x;
   const int e_base = t * kpt4;
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(row);
@@ -168,6 +169,10 @@ __device__ __forceinline__ void load_keys_blocked(const float* row, int n, int c
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[i][j] = keys[i][j];
   if (e_base + kpt4 <= n) {  // every entry of the thread is in the row (all but the last threads)
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
@@ -514,8 +519,9 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   };
 
   uint32_t keys[SLOTS][4];
+  uint32_t raw[BLOCKED ? SLOTS : 1][4];  // blocked rows: the scores' bits as loaded
   if constexpr (BLOCKED)
-    load_keys_blocked<NT, SLOTS, COHERENT>(row, n, cap, kpt4, keys);
+    load_keys_blocked<NT, SLOTS, COHERENT>(row, n, cap, kpt4, keys, raw);
   else if (cached)
     load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
 
@@ -587,15 +593,16 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         if (!slot_live(0, i)) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t key = keys[i][j];
-          const float x = __builtin_fmaf(key_to_score(key), scale, off);
-          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1));
+          // unscored entries (kKeyNegInf, or past the row with arbitrary
+          // bits) go to bin 0 and are not counted
+          const bool act = keys[i][j] != kKeyNegInf;
+          const float x = __builtin_fmaf(__uint_as_float(raw[i][j]), scale, off);
+          const uint32_t bin = act ? (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1)) : 0u;
           bins[i][j] = bin;
           // Spread-out bins rarely collide within a wave, so lanes add their
           // own counts; a wave whose active lanes all share one bin (clustered
           // rows; active lanes are a prefix of the wave, so lane 0 is one of
           // them) adds them with one atomic instead of 64 serialised ones.
-          const bool act = key != kKeyNegInf;
           const uint64_t m = ballot(act);
           if (m != 0) {
             const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
