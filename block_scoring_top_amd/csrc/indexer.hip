@@ -32,9 +32,10 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
   const int r1 = min(r_end, nv);
   float* dst = scores + (size_t)b * N_pad;
   if (r1 > r0) {
-    float qs[8];
-    load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
-    score_rows<BF16, kScoreNT>(c, DenseRows{(size_t)b * N_pad}, qs, r0, r1, dst);
+    QHeads<BF16> qh;
+    qh.issue(q, b, H, 0, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
+    score_rows<BF16, kScoreNT>(table_of<BF16>(c, (size_t)b * N_pad), DenseRows{}, qh, q, b, H,
+                               r0, r1, dst);
   }
   fill_neg_inf(dst, max(r0, nv), r_end);
 }
@@ -122,9 +123,10 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x - b * nchunk;
-  // the summed query and the request length are loaded together (one round trip)
-  float qs[8];
-  load_qsum<BF16>(q, b, H, threadIdx.x & 15, qs);
+  // the first query heads are requested with the request length, and summed
+  // while the first centroid rows are in flight
+  QHeads<BF16> qh;
+  qh.issue(q, b, H, 0, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
   int nv;
   int64_t pbase = 0, avail = 0;
   if constexpr (PAGED) {
@@ -150,9 +152,10 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     constexpr int U = NT >= 1024 ? 2 : 4;
     if constexpr (PAGED)
       score_rows<BF16, NT, true, U>(c, PagedRows{indices + (avail > 0 ? pbase : 0), avail, n_rows},
-                                    qs, r0, r1, row);
+                                    qh, q, b, H, r0, r1, row);
     else
-      score_rows<BF16, NT, true, U>(c, DenseRows{(size_t)b * N_pad}, qs, r0, r1, row);
+      score_rows<BF16, NT, true, U>(table_of<BF16>(c, (size_t)b * N_pad), DenseRows{}, qh, q, b,
+                                    H, r0, r1, row);
   }
   if (scores_out != nullptr) fill_neg_inf(row, max(r0, nv), r_end);
 

@@ -252,30 +252,6 @@ __host__ __device__ inline int sort_lds_bytes(int K) {
   return p * 8;
 }
 
-// The value of lane (lane ^ M) for M a power of two below 64, without LDS:
-// DPP within a 16-lane row (quad permutes, row shifts, row rotation) and the
-// gfx950 row-swap permutes across rows.
-template <int M>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (M == 1) {
-    return dpp_u32<kDppQuadXor1>(v);
-  } else if constexpr (M == 2) {
-    return dpp_u32<kDppQuadXor2>(v);
-  } else if constexpr (M == 4) {
-    const uint32_t up = dpp_u32<kDppRowShl1 + 3>(v);  // lane l + 4
-    const uint32_t dn = dpp_u32<kDppRowShr1 + 3>(v);  // lane l - 4
-    return (lane_id() & 4) ? dn : up;
-  } else if constexpr (M == 8) {
-    return dpp_u32<kDppRowRor1 + 7>(v);  // rotation by 8 within the row
-  } else if constexpr (M == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane_id() & 16) ? r[0] : r[1];
-  } else {
-    static_assert(M == 32, "lane distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane_id() & 32) ? r[0] : r[1];
-  }
-}
 template <int M>
 __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
   return (uint64_t)lane_xor<M>((uint32_t)(v >> 32)) << 32 | lane_xor<M>((uint32_t)v);
