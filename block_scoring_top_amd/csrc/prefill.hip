@@ -98,32 +98,47 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
   // hi + lo, and stores both at slot k * 32 + u, so that a wave's operand read
   // (32 tokens, one chunk) is 512 contiguous bytes.
   __shared__ uint4 a_hi[16 * kPfTok], a_lo[16 * kPfTok];
+  constexpr int kItems = 16 * kPfTok / kPfNT;  // items per thread
+  // the first four heads of every item are requested before any is added
+  // (tokens past T read token T - 1 and add nothing; heads past H add nothing)
+  uint4 v[kItems][4];
 #pragma unroll
-  for (int it = 0; it < 16 * kPfTok / kPfNT; ++it) {
+  for (int it = 0; it < kItems; ++it) {
+    const int item = it * kPfNT + threadIdx.x;
+    const int t = min(t0 + (item >> 4), T - 1);
+    const uint4* qt = reinterpret_cast<const uint4*>(q + ((size_t)b * T + t) * H * kHeadDim) + (item & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[it][i] = qt[(size_t)min(i, H - 1) * 16];
+  }
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
     const int item = it * kPfNT + threadIdx.x;
     const int u = item >> 4, k = item & 15;
-    const int t = t0 + u;
+    const bool live_t = t0 + u < T;
+    const uint4* qt =
+        reinterpret_cast<const uint4*>(q + ((size_t)b * T + min(t0 + u, T - 1)) * H * kHeadDim) + k;
     float sum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-    if (t < T) {
-      const uint4* qt = reinterpret_cast<const uint4*>(q + ((size_t)b * T + t) * H * kHeadDim) + k;
-      // four heads per step: their loads are in flight together
-      for (int h0 = 0; h0 < H; h0 += 4) {
-        uint4 v[4];
+    auto add4 = [&](const uint4 (&w4)[4], int h0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = qt[(size_t)(h0 + i < H ? h0 + i : H - 1) * 16];
+      for (int i = 0; i < 4; ++i) {
+        const bool live = live_t && h0 + i < H;
+        const uint32_t wd[4] = {w4[i].x, w4[i].y, w4[i].z, w4[i].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (h0 + i >= H) break;
-          const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sum[2 * e] += bf16_lo(wd[e]);
-            sum[2 * e + 1] += bf16_hi(wd[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          sum[2 * e] += live ? bf16_lo(wd[e]) : 0.f;
+          sum[2 * e + 1] += live ? bf16_hi(wd[e]) : 0.f;
         }
       }
+    };
+    add4(v[it], 0);
+    // more heads: four per step, their loads in flight together
+    for (int h0 = 4; h0 < H; h0 += 4) {
+      uint4 w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[i] = qt[(size_t)min(h0 + i, H - 1) * 16];
+      add4(w4, h0);
     }
     uint32_t h4[4], l4[4];
 #pragma unroll
