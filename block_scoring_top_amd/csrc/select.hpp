@@ -501,17 +501,24 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   else if (cached)
     load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
 
-  // The all-equal exits need the min and max of the keys in play: after the
-  // first pass those of the row (blocked rows take them here, once, and the
-  // max may include inactive keys: kKeyNegInf is below every active key but
-  // negative NaNs, so min == max still means all active keys are equal), and
-  // for striped rows (idx_topk inputs: quantised, heavy-tailed or tied rows)
-  // after the second pass those of the keys left in the chosen bins. The
-  // blocked rows of the fused select (dot-product scores) skip that second
-  // range: its cost on every row outweighs the pass it saves on tied rows,
-  // and the third pass resolves every remaining bit either way.
+  // The linear bins and the all-equal exits need the min and max of the keys
+  // in play: after the first pass those of the row (rows that try the linear
+  // bins take them here, once, others during the first pass; the max may
+  // include inactive keys: kKeyNegInf is below every active key but negative
+  // NaNs, so min == max still means all active keys are equal), and for
+  // striped rows (idx_topk inputs: quantised, heavy-tailed or tied rows) after
+  // the second pass those of the keys left in the chosen bins. The blocked
+  // rows of the fused select (dot-product scores) skip that second range: its
+  // cost on every row outweighs the pass it saves on tied rows, and the third
+  // pass resolves every remaining bit either way.
+  // Rows held in registers first try one pass over linear value bins (below),
+  // except in the 8-slot instances (few long idx_topk rows, any distribution):
+  // on quantised or tied rows the wasted pass costs more (measured: 30.5 ->
+  // 40 us on the top-K stress rows) than it saves on spread-out ones.
+  constexpr bool kLinear = BLOCKED || SLOTS <= 2;
+  const bool upfront = kLinear && cached;  // the range is taken before the passes
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  if (BLOCKED) {
+  if (upfront) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       if (!slot_live(0, i)) continue;
@@ -541,7 +548,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   uint32_t t_lo = 0u;
   int boff = 0;  // histogram buffer of the first radix pass
 
-  // Blocked rows first try one pass over linear value bins: with the row's
+  // The linear pass: with the row's
   // range [lo, hi], key x goes to bin floor((x - lo) * kBins / (hi - lo)),
   // clamped to the last bin (monotone in x, so a higher bin never holds a
   // smaller key). On spread-out scores the bin of the K-th key then holds a
@@ -550,7 +557,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   // bin holds at most 64 keys, they are gathered in LDS and wave 0 ranks them:
   // the threshold is then an exact key. Otherwise (ranges that are not finite,
   // clustered or tied rows) the radix passes below resolve the row.
-  if constexpr (BLOCKED) {
+  if (upfront) {
     uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
     uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
     lo = wave_reduce_minmax<true>(lo);
@@ -572,13 +579,19 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           // unscored entries (kKeyNegInf, or past the row with arbitrary
           // bits) go to bin 0 and are not counted
           const bool act = keys[i][j] != kKeyNegInf;
-          const float x = __builtin_fmaf(__uint_as_float(raw[i][j]), scale, off);
+          float f;
+          if constexpr (BLOCKED)
+            f = __uint_as_float(raw[i][j]);
+          else
+            f = key_to_score(keys[i][j]);
+          const float x = __builtin_fmaf(f, scale, off);
           const uint32_t bin = act ? (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1)) : 0u;
           bins[i][j] = bin;
           // Spread-out bins rarely collide within a wave, so lanes add their
-          // own counts; a wave whose active lanes all share one bin (clustered
-          // rows; active lanes are a prefix of the wave, so lane 0 is one of
-          // them) adds them with one atomic instead of 64 serialised ones.
+          // own counts; a wave whose active lanes all share lane 0's bin
+          // (clustered rows: active lanes are a prefix of the wave unless the
+          // row holds -inf scores, and an inactive lane 0 has bin 0) adds them
+          // with one atomic instead of 64 serialised ones.
           const uint64_t m = ballot(act);
           if (m != 0) {
             const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
@@ -685,7 +698,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     const int shift = digit_shift(p);
     const uint32_t dmask = digit_mask(p);
     const int hshift = p == 0 ? 0 : digit_shift(p - 1);  // the resolved bits sit above this
-    const bool track = !BLOCKED && p <= 1;  // this pass takes the range of its keys
+    // this pass takes the range of its keys
+    const bool track = (p == 0 && !upfront) || (!BLOCKED && p == 1);
     if (p == 1) {
       kmin = 0xFFFFFFFFu;
       kmax = 0u;
