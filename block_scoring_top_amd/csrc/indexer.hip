@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------
+constexpr int kPageStage = 256;  // page-list entries a paged chunk stages in LDS (default chunks <= 256)
 // NT threads per workgroup, select tile NT*SLOTS*4 keys.
 // PAGED: request b's score slots are its page list indices[indptr[b] ..
 // indptr[b+1]) (at most N_pad of them) into a shared pool of n_rows centroids;
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     const int32_t* __restrict__ indices, int64_t n_indices, int n_rows) {
   __shared__ SelectSmem<NT, SLOTS> sm;
   __shared__ int s_last;
+  __shared__ int32_t s_pages[PAGED ? kPageStage : 1];
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x - b * nchunk;
@@ -150,10 +152,19 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   const int r1 = min(r_end, nv);
   if (r1 > r0) {
     constexpr int U = NT >= 1024 ? 2 : 4;
-    if constexpr (PAGED)
-      score_rows<BF16, NT, true, U>(c, PagedRows{indices + (avail > 0 ? pbase : 0), avail, n_rows},
-                                    qh, q, b, H, r0, r1, row);
-    else
+    if constexpr (PAGED) {
+      // The chunk's page-list entries, validated, are staged in LDS (one round
+      // trip per kPageStage of them), so that a row load waits on an LDS read
+      // only: a list load would also wait for every row load issued before it.
+      const PagedRows pages{indices + (avail > 0 ? pbase : 0), avail, n_rows};
+      for (int s0 = r0; s0 < r1; s0 += kPageStage) {
+        const int s1 = min(s0 + kPageStage, r1);
+        if (s0 > r0) __syncthreads();  // the previous piece's entries are read
+        for (int i = threadIdx.x; i < s1 - s0; i += NT) s_pages[i] = pages(s0 + i);
+        __syncthreads();
+        score_rows<BF16, NT, true, U>(c, StagedRows{s_pages, s0}, qh, q, b, H, s0, s1, row);
+      }
+    } else
       score_rows<BF16, NT, true, U>(table_of<BF16>(c, (size_t)b * N_pad), DenseRows{}, qh, q, b,
                                     H, r0, r1, row);
   }

@@ -114,6 +114,14 @@ struct PagedRows {
   }
 };
 
+// Paged rows whose validated table rows (or -1) were staged in LDS: slot r of
+// the request is staged[r - base].
+struct StagedRows {
+  const int32_t* staged;
+  int base;
+  __device__ __forceinline__ int operator()(int r) const { return staged[r - base]; }
+};
+
 // The centroid table that starts `rows` rows into c.
 template <bool BF16>
 __device__ __forceinline__ const void* table_of(const void* c, size_t rows) {

@@ -104,6 +104,32 @@ def test_paged_lists_past_the_index_array_and_clamped_counts():
     full_paged_check(x, indptr=indptr, max_pages=200)
 
 
+@pytest.mark.parametrize("chunk_log2", [10, 12])
+def test_paged_large_chunks_stage_their_lists_in_pieces(chunk_log2):
+    """Chunks of 1024 and 4096 slots stage their page lists 256 entries at a
+    time: the same ids and scores as the default chunking, and the oracle's,
+    with invalid entries among the staged ones."""
+    x = synth.make_paged(3, 4, 128, 5000, [4500, 3000, 1300], 200, "bf16", 615, name="chunks")
+    indices = x.indices.copy()
+    indices[300] = -1
+    indices[4500 + 2999] = 5000
+    mp = x.max_pages
+    say(f"[paged] large chunks 2^{chunk_log2}")
+    args = (to_dev(x.q), to_dev(x.c_pool), to_dev(x.indptr.astype(np.int32)),
+            to_dev(indices.astype(np.int32)), 200, mp)
+    ids, counts, s = idx.idx_select_paged(*args, return_scores=True, chunk_log2=chunk_log2)
+    ids_d, counts_d, s_d = idx.idx_select_paged(*args, return_scores=True)
+    torch.cuda.synchronize()
+    ids, counts, s = ids.cpu().numpy(), counts.cpu().numpy(), s.cpu().numpy()
+    S, A, n_slots = oracle.score_paged(x.q, x.c_pool, x.indptr, indices, mp, x.dtype)
+    check_scores(s, S, A, RTOL[x.dtype])
+    check_ids_exact(ids, counts, s, n_slots, 200, False)
+    np.testing.assert_array_equal(ids, ids_d.cpu().numpy())
+    np.testing.assert_array_equal(counts, counts_d.cpu().numpy())
+    np.testing.assert_array_equal(s.view(np.uint32), s_d.cpu().numpy().view(np.uint32))
+    assert s[0, 300] == -np.inf and s[1, 2999] == -np.inf
+
+
 def test_paged_identity_lists_equal_the_dense_call():
     """Identity page lists over a per-request table: the same ids, counts and
     scores, bit for bit, as idx_select on the dense table."""
