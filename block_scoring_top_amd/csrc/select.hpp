@@ -5,12 +5,6 @@
 // cached in registers for short rows). Ties are taken in ascending index order,
 // which the pages' bitwise id checks with adversarial ties require.
 //
-// Digits here are 11, 11 and 10 bits (three passes instead of the pages' four
-// 8-bit ones: a 2048-bin histogram is 8 KiB of LDS, and every pass costs a few
-// barriers, which dominate at these row lengths). A pass stops the select
-// early when the chosen bin is taken whole, or when every key still in play is
-// the same value.
-//
 // One workgroup of NT threads selects one row. Keys live in registers, in one
 // of two layouts. Striped: slot i of thread t holds the 4 consecutive entries
 // starting at 4*(i*NT + t), so every load is a coalesced 16-byte vector load
@@ -18,17 +12,31 @@
 // tile by tile each pass. Blocked: thread t holds one run of consecutive
 // entries, which makes the emit a single scan (rows that fit one tile).
 //
-// Histogram: one 2048-bin histogram in LDS (two, alternating by pass, so one is
-// cleared while the other is read). Before the LDS atomics a wave peels off the
-// group of lanes that share the first active lane's digit and adds that group
-// with one atomic; on degenerate rows (all equal, few distinct values) this
-// removes the same-address atomic serialisation.
+// The select is bound by the issue of its per-key vector instructions (up to
+// 16 waves share one CU) and by its barriers, so it is built to touch each key
+// as few times, with as few instructions, as it can:
+//  - Linear first pass (rows held in registers, except the 8-slot instances):
+//    keys are counted in 2048 bins spread linearly over the row's value range.
+//    On spread-out scores the K-th key's bin then holds a few keys: taken
+//    whole, its smallest key is the threshold; otherwise up to 64 of them are
+//    gathered in LDS and ranked. Rows where this fails (range not finite,
+//    clustered or tied rows) fall back to:
+//  - Radix passes: digits of 11, 11 and 10 bits (three passes instead of the
+//    pages' four 8-bit ones; a 2048-bin histogram is 8 KiB of LDS). A pass
+//    stops early when the chosen bin is taken whole, or when every key still
+//    in play is the same value.
+// Histograms: two 2048-bin LDS histograms, alternating by pass, so one is
+// cleared while the other is searched; the search runs in all waves. Histogram
+// adds peel off lanes that share a bin (a whole wave, or 16 or more lanes with
+// the first active lane's digit) into one atomic, which removes the
+// same-address atomic serialisation of degenerate rows.
 //
-// Emit: a key is taken if its resolved digits exceed the threshold prefix, or
-// equal it and fewer than `need` equal keys precede it. Output positions come
-// from in-wave counts plus one workgroup scan, so ids are written in ascending
-// index order without atomics (deterministic). The score order (score desc,
-// id asc) is a bitonic sort of the selected (key, ~id) pairs as 64-bit words.
+// Emit: the taken keys are given by two bounds on a class value (the key, or
+// the linear bin): above the upper bound taken, between the bounds the first
+// `need` in index order. Output positions come from in-wave counts plus one
+// workgroup scan, so ids are written in ascending index order without atomics
+// (deterministic). The score order (score desc, id asc) is a bitonic sort of
+// the selected (key, ~id) pairs as 64-bit words.
 #pragma once
 
 #include "common.hpp"
@@ -48,8 +56,8 @@ struct SelectSmem {
   static constexpr int NW = NT / kWave;
   static constexpr int E = SLOTS * NW;  // emit-count entries per tile
   alignas(16) uint32_t hist[2][kBins];
-  uint32_t wpack[NW];  // per-wave packed (eq << 16 | gt) counts of the blocked emit
-  uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the row's active keys
+  uint32_t wpack[NW];  // per-wave counts of the blocked emit
+  uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the keys in play
   uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
   uint32_t n_gather, gather[kWave];  // the keys of a small threshold bin
   uint32_t wtot[NW];                 // per-wave bin totals of the bin search
@@ -480,8 +488,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
   constexpr int E = SLOTS * NW;
-  static_assert(NT >= 256 && NT % 256 == 0, "at least four waves; histogram clears use waves 1..");
-  static_assert(kBins == 32 * kWave, "the bin search gives each lane of wave 0 32 bins");
+  static_assert(NT >= 256 && NT <= 1024 && NT % 256 == 0,
+                "256 to 1024 threads: the bin search gives each thread 2 to 8 bins");
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
@@ -542,21 +550,22 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
   int level = 0;  // digits resolved (kPasses = the whole key)
   bool take_all = false, resolved = false;
-  // simple threshold: exactly the keys whose class value (the key, or below
-  // the linear bin) is at least t_lo are taken, with no partial tie
+  // simple threshold: exactly the keys whose class value (the key, or its
+  // linear bin) is at least t_lo are taken, with no partial tie
   bool simple = false;
   uint32_t t_lo = 0u;
   int boff = 0;  // histogram buffer of the first radix pass
 
-  // The linear pass: with the row's
-  // range [lo, hi], key x goes to bin floor((x - lo) * kBins / (hi - lo)),
-  // clamped to the last bin (monotone in x, so a higher bin never holds a
-  // smaller key). On spread-out scores the bin of the K-th key then holds a
-  // few keys, where the first 11-bit digit (sign, exponent, two mantissa bits)
-  // leaves tens to hundreds, and a second radix pass would follow. When that
-  // bin holds at most 64 keys, they are gathered in LDS and wave 0 ranks them:
-  // the threshold is then an exact key. Otherwise (ranges that are not finite,
-  // clustered or tied rows) the radix passes below resolve the row.
+  // The linear pass: with the row's range [lo, hi], key x goes to bin
+  // floor((x - lo) * kBins / (hi - lo)), clamped to the last bin (monotone in
+  // x, so a higher bin never holds a smaller key, and equal scores share a
+  // bin). On spread-out scores the bin of the K-th key then holds a few keys,
+  // where the first 11-bit digit (sign, exponent, two mantissa bits) leaves
+  // tens to hundreds, and a second radix pass would follow. A bin taken whole
+  // gives a simple threshold; a bin of at most 64 keys is gathered in LDS and
+  // wave 0 ranks them, which gives an exact threshold key. Otherwise (ranges
+  // that are not finite, clustered or tied rows) the radix passes below
+  // resolve the row.
   if (upfront) {
     uint32_t lo = lane < NW ? sm.wmin[lane] : 0xFFFFFFFFu;
     uint32_t hi = lane < NW ? sm.wmax[lane] : 0u;
