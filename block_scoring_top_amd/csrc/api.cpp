@@ -230,8 +230,9 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
                                       round_up((size_t)rows * sizeof(int32_t), 256));
     stride = stage_stride(N_pad);
   }
+  // staged scores are read only up to each token's count: no -inf fill
   int e = idxk::launch_prefill_score(q, c, pos0, scores, stride, n_valid, B, T, H, N_pad,
-                                     page_size, stream);
+                                     page_size, scores_out != nullptr, stream);
   if (e != 0) return IDX_ERR_HIP;
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, (int)rows, (int)stride, K,
                                       sorted, nullptr, stream));

@@ -39,6 +39,6 @@ int launch_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int 
 // (row_stride >= N_pad) and each token's visible block count into n_valid[b*T + t].
 int launch_prefill_score(const void* q, const void* c, const int32_t* pos0, float* scores,
                          int64_t row_stride, int32_t* n_valid, int B, int T, int H, int N_pad,
-                         int page_size, void* stream);
+                         int page_size, bool fill_dead, void* stream);
 
 }  // namespace idxk

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ c,
     const int32_t* __restrict__ pos0, float* __restrict__ scores, int64_t row_stride,
     int32_t* __restrict__ n_valid_out, int T, int H, int N_pad, int page_size, int n_ttiles,
-    int n_ctiles) {
+    int n_ctiles, bool fill_dead) {
   const int per_b = n_ttiles * n_ctiles;
   const int b = blockIdx.x / per_b;
   const int rem = blockIdx.x - b * per_b;
@@ -67,9 +67,11 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
   // blocks visible to the tile's last token bound every token of the tile
   const int nv_max = prefill_n_valid(p0, min(t0 + kPfTok, T) - 1, page_size, N_pad);
   float* out = scores + (size_t)b * T * row_stride;
-  // columns no token of the tile sees get -inf; a workgroup with none visible
-  // at all leaves at once (the condition is the same for all its waves)
-  auto fill_dead = [&]() {
+  // columns no token of the tile sees get -inf when the scores are the
+  // caller's output (staged scores past a token's count are never read); a
+  // workgroup with none visible at all leaves at once (the condition is the
+  // same for all its waves)
+  auto fill_dead_cols = [&]() {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
     }
   };
   if (ct * kPfCols >= nv_max) {
-    fill_dead();
+    if (fill_dead) fill_dead_cols();
     return;
   }
   const bool live = n0 < nv_max;  // this wave's 32 columns hold a visible block
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
   __syncthreads();
 
   if (!live) {
-    fill_dead();
+    if (fill_dead) fill_dead_cols();
     return;
   }
   pf_f32x16 acc;
@@ -178,13 +180,14 @@ __global__ __launch_bounds__(kPfNT) void prefill_score_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (t < T && n < N_pad) out[(size_t)t * row_stride + n] = start <= t ? acc[r] : -__builtin_inff();
+    if (t < T && n < N_pad && (fill_dead || start <= t))
+      out[(size_t)t * row_stride + n] = start <= t ? acc[r] : -__builtin_inff();
   }
 }
 
 int launch_prefill_score(const void* q, const void* c, const int32_t* pos0, float* scores,
                          int64_t row_stride, int32_t* n_valid, int B, int T, int H, int N_pad,
-                         int page_size, void* stream) {
+                         int page_size, bool fill_dead, void* stream) {
   const int n_ttiles = (T + kPfTok - 1) / kPfTok;
   const int n_ctiles = (N_pad + kPfCols - 1) / kPfCols;
   const int64_t grid = (int64_t)B * n_ttiles * n_ctiles;
@@ -192,7 +195,7 @@ int launch_prefill_score(const void* q, const void* c, const int32_t* pos0, floa
   hipLaunchKernelGGL(prefill_score_kernel, dim3((unsigned)grid), dim3(kPfNT), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(c), pos0, scores, row_stride, n_valid, T, H,
-                     N_pad, page_size, n_ttiles, n_ctiles);
+                     N_pad, page_size, n_ttiles, n_ctiles, fill_dead);
   return (int)hipGetLastError();
 }
 

@@ -208,13 +208,14 @@ __device__ __forceinline__ void load_keys_blocked(const float* row, int n, int c
 __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t digit) {
   const uint64_t m = ballot(act);
   if (m == 0) return;
-  const int leader = __builtin_ctzll(m);
-  const uint32_t d0 = readlane<uint32_t>(digit, leader);
-  const uint64_t same = ballot(act && digit == d0);
+  const uint32_t d0 = readlane<uint32_t>(digit, __builtin_ctzll(m));
+  const uint64_t same = ballot(digit == d0) & m;
   const uint32_t ns = popc64(same);
   if (ns >= 16) {
-    const bool is_leader = lane_id() == leader;
-    if (act && (digit != d0 || is_leader)) atomicAdd(&h[digit], is_leader ? ns : 1u);
+    // the group's other lanes skip; its first lane adds the group's count
+    const uint64_t lead = m & (~m + 1);
+    if (__builtin_amdgcn_inverse_ballot_w64((m & ~same) | lead))
+      atomicAdd(&h[digit], __builtin_amdgcn_inverse_ballot_w64(lead) ? ns : 1u);
   } else if (act) {
     atomicAdd(&h[digit], 1u);
   }
