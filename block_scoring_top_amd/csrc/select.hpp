@@ -35,8 +35,11 @@
 // the linear bin): above the upper bound taken, between the bounds the first
 // `need` in index order. Output positions come from in-wave counts plus one
 // workgroup scan, so ids are written in ascending index order without atomics
-// (deterministic). The score order (score desc, id asc) is a bitonic sort of
-// the selected (key, ~id) pairs as 64-bit words.
+// (deterministic). The score order (score desc, id asc) orders the selected
+// (key, ~id) pairs as 64-bit words: when the linear pass settled the row with a
+// simple threshold, each taken key goes straight to its bin's segment of the
+// output (counts of the bins above it, plus a slot from one LDS atomic) and
+// ranks itself among the few keys of its bin; otherwise a bitonic sort.
 #pragma once
 
 #include "common.hpp"
@@ -420,6 +423,47 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
   }
 }
 
+// The linear bin of a key: the same float arithmetic as the linear pass (the
+// key's score, scaled and shifted, clamped to [0, kBins - 1]).
+struct BinMap {
+  float scale, off;
+  __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
+    const float x = __builtin_fmaf(key_to_score(key), scale, off);
+    return (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1));
+  }
+};
+
+// Finishes the score order of m pairs that sit in sortbuf[0..m) grouped by
+// linear bin, highest bin first: bin b's pairs fill [sfx[b], sfx[b] + cnt[b]) in
+// no particular order. Each thread takes the pairs at positions t + e * NT,
+// ranks each among the pairs of its bin (one or two on spread-out scores; four
+// reads in flight at a time) and hands the final position to out.put.
+template <int NT, int E, typename Out>
+__device__ __forceinline__ void rank_in_bins(uint64_t* sortbuf, int m, const BinMap& bin_of,
+                                             const uint32_t* cnt, const uint32_t* sfx,
+                                             const Out& out) {
+  const int t = threadIdx.x;
+  __syncthreads();  // every pair is in place
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = t + e * NT;
+    if (i < m) {
+      const uint64_t v = sortbuf[i];
+      const uint32_t key = (uint32_t)(v >> 32), b = bin_of(key);
+      const uint32_t base = sfx[b], c = cnt[b];
+      uint32_t rank = 0;
+      for (uint32_t r0 = 0; r0 < c; r0 += 4) {
+        uint64_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = sortbuf[min(base + r0 + u, (uint32_t)m - 1u)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += (r0 + u < c && x[u] > v) ? 1u : 0u;
+      }
+      out.put((int)(base + rank), (int32_t)~(uint32_t)v, key);
+    }
+  }
+}
+
 // All NW waves find the bin of h that holds the need-th largest of the counted
 // keys, bins ranked from the top (kBins - 1) down: sm.sel_bin, sm.sel_need
 // (need minus the keys in higher bins), sm.sel_tot (the bin's count) and
@@ -430,10 +474,12 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
 // scan of the per-wave totals gives the counts above each wave. The lane whose
 // run holds the need-th key then walks its bins. Ends with a barrier; the
 // results are read after the caller's next barrier. `clear` (may be null),
-// kBins words, is zeroed on the way.
+// kBins words, is zeroed on the way. With `sfx` (kBins words, may be null),
+// sfx[b] gets the count of the bins above b and h is zeroed (for reuse as
+// per-bin counters).
 template <int NT, class SM>
-__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, SM& sm,
-                                         uint32_t* clear) {
+__device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uint32_t* clear,
+                                         uint32_t* sfx = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int BPL = kBins / NT;  // bins per lane: 2, 4 or 8
   static_assert(BPL == 2 || BPL == 4 || BPL == 8, "2048 bins over 256..1024 threads");
@@ -460,11 +506,23 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, SM& s
 #pragma unroll
     for (int k = 0; k < BPL; ++k) clear[threadIdx.x * BPL + k] = 0u;
   }
+  if (sfx != nullptr) {  // this lane's own bins, already read
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) h[top - 1 - k] = 0u;
+  }
   __syncthreads();
   const uint32_t ws = wave_incl_scan(lane < NW ? sm.wtot[lane] : 0u);
   const uint32_t above = w > 0 ? readlane<uint32_t>(ws, w - 1) : 0u;
   if (w == 0 && lane == 0) sm.n_cand = readlane<uint32_t>(ws, NW - 1);
   uint32_t cum = above + incl - loc;
+  if (sfx != nullptr) {
+    uint32_t run = cum;
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      sfx[top - 1 - k] = run;
+      run += c[k];
+    }
+  }
   if (cum < need && need <= cum + loc) {  // one lane: the need-th key is in its bins
 #pragma unroll
     for (int k = 0; k < BPL; ++k) {
@@ -556,6 +614,12 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   bool simple = false;
   uint32_t t_lo = 0u;
   int boff = 0;  // histogram buffer of the first radix pass
+  // score order from the linear bins (SORTED rows the linear pass settles
+  // with a simple threshold): histogram 1 holds the count of the keys in
+  // higher bins, histogram 0 per-bin counters
+  bool by_bins = false;
+  uint32_t bins[SLOTS][4];
+  float bin_scale = 0.f, bin_off = 0.f;  // a key's bin: fmed3(fma(score, scale, off), 0, kBins - 1)
 
   // The linear pass: with the row's range [lo, hi], key x goes to bin
   // floor((x - lo) * kBins / (hi - lo)), clamped to the last bin (monotone in
@@ -579,8 +643,9 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     if (lo < hi && __builtin_isfinite(flo) && __builtin_isfinite(fhi) &&
         __builtin_isfinite(span) && span > 0.f && __builtin_isfinite(scale)) {
       const float off = -flo * scale;
+      bin_scale = scale;
+      bin_off = off;
       uint32_t* h = sm.hist[0];
-      uint32_t bins[SLOTS][4];
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
         if (!slot_live(0, i)) continue;
@@ -618,13 +683,17 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         sm.same_key = 0xFFFFFFFFu;
       }
       __syncthreads();
-      find_bin<NT>(h, need, sm, sm.hist[1]);
+      if constexpr (SORTED)
+        find_bin<NT>(h, need, sm, nullptr, sm.hist[1]);
+      else
+        find_bin<NT>(h, need, sm, sm.hist[1]);
       __syncthreads();
       ncand = sm.n_cand;
       const uint32_t sb = sm.sel_bin, bneed = sm.sel_need, btot = sm.sel_tot;
       if (ncand <= (uint32_t)K) {
         take_all = true;
         resolved = true;
+        by_bins = SORTED;
       } else if (btot == bneed && !SORTED && !Out::kUsesKey && sb > 0) {
         // the bin is taken whole and only ids are written: the keys of bins
         // sb and above are taken, so the bins become the class values (scored
@@ -650,6 +719,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         simple = true;
         t_lo = sm.same_key;
         resolved = true;
+        by_bins = SORTED;
       } else if (btot <= (uint32_t)kWave) {
         // gather the bin's keys: one slot reservation per wave and key slot
 #pragma unroll
@@ -683,9 +753,11 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           const int l0 = hm != 0 ? __builtin_ctzll(hm) : 0;  // hm != 0: 1 <= bneed <= btot
           const uint32_t tkey = readlane<uint32_t>(c, l0);
           const uint32_t tgt = readlane<uint32_t>(gt, l0);
+          const uint32_t teq = readlane<uint32_t>(eq, l0);
           if (lane == 0) {
             sm.same_key = tkey;
             sm.sel_need = bneed - tgt;
+            sm.all_same = teq == bneed - tgt ? 1u : 0u;  // every copy of the threshold taken
           }
         }
         __syncthreads();
@@ -693,8 +765,15 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         need = sm.sel_need;
         level = kPasses;
         resolved = true;
+        if (sm.all_same) {
+          simple = true;
+          t_lo = prefix;
+          by_bins = SORTED;
+        }
       } else {
-        boff = 1;  // histogram 0 holds the linear counts; histogram 1 is clear
+        // the linear counts are in histogram 0 and histogram 1 is clear, or
+        // (score-ordered rows) histogram 0 was zeroed for counters
+        boff = SORTED ? 0 : 1;
       }
     }
   }
@@ -793,7 +872,38 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   const uint32_t hi_b = simple ? t_lo - 1u : lo_b | ((1u << shiftL) - 1u);
   const uint32_t need_e = simple ? 0u : need;
   const uint32_t m_out = take_all ? ncand : (uint32_t)K;
-  if constexpr (BLOCKED) {
+  if constexpr (SORTED) {
+    if (by_bins) {
+      // Score order from the linear bins, no sorting network: histogram 1
+      // holds sfx[b], the count of the taken keys in bins above b, and
+      // histogram 0 is zero. A taken key of bin b goes to slot sfx[b] +
+      // atomicAdd(cnt[b], 1) (every atomic of the thread issued before the
+      // first return is used); rank_in_bins then orders each bin's keys.
+      uint32_t* cnt = sm.hist[0];
+      const uint32_t* sfx = sm.hist[1];
+      uint32_t dst[SLOTS][4];
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dst[i][j] = 0u;
+          if (keys[i][j] >= t_lo) dst[i][j] = atomicAdd(&cnt[bins[i][j]], 1u) + sfx[bins[i][j]];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (!slot_live(0, i)) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int id = BLOCKED ? t * kpt4 + 4 * i + j : (i * NT + t) * 4 + j;
+          if (keys[i][j] >= t_lo && dst[i][j] < m_out)  // dst < m_out always holds
+            sortbuf[dst[i][j]] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
+        }
+      }
+    }
+  }
+  if (BLOCKED && !by_bins) {
     // Blocked layout: each thread counts its taken-for-sure (gt) and threshold
     // (eq) keys, one workgroup scan of the counts gives the keys before the
     // thread, and the thread then writes its taken ids in ascending order.
@@ -872,7 +982,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     }
   }
   uint32_t carry_gt = 0, carry_eq = 0;
-  for (int tile = 0; tile < (BLOCKED ? 0 : ntiles); ++tile) {
+  for (int tile = 0; tile < ((BLOCKED || by_bins) ? 0 : ntiles); ++tile) {
     if (!cached) {
       __syncthreads();  // the previous tile's counts have been read
       load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
@@ -936,18 +1046,29 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   if (count_out != nullptr && t == 0) *count_out = (int32_t)m_out;
 
   if constexpr (SORTED) {
-    // (key << 32 | ~id) is unique per pair and orders by key, then by lower id;
-    // zero (below every key) pads the sort up to a power of two
+    // (key << 32 | ~id) is unique per pair and orders by key, then by lower id
     int P = 2;
     while (P < (int)m_out) P <<= 1;
-    if (P <= NT) {
-      sort_pairs_desc<NT, 1>(sortbuf, (int)m_out, P, out);
-    } else if (P == 2 * NT) {
-      sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, out);
+    // P <= 4 * NT: callers give 256- and 512-thread workgroups at most 1024 ids
+    // to order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
+    if (by_bins) {
+      const BinMap bm{bin_scale, bin_off};
+      if (P <= NT) {
+        rank_in_bins<NT, 1>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+      } else if (P == 2 * NT) {
+        rank_in_bins<NT, 2>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+      } else {
+        rank_in_bins<NT, 4>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+      }
     } else {
-      // P == 4 * NT: callers give 256- and 512-thread workgroups at most 1024
-      // ids to order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
-      sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, out);
+      // zero (below every key) pads the sort up to a power of two
+      if (P <= NT) {
+        sort_pairs_desc<NT, 1>(sortbuf, (int)m_out, P, out);
+      } else if (P == 2 * NT) {
+        sort_pairs_desc<NT, 2>(sortbuf, (int)m_out, P, out);
+      } else {
+        sort_pairs_desc<NT, 4>(sortbuf, (int)m_out, P, out);
+      }
     }
   }
 }
