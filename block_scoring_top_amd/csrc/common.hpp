@@ -141,6 +141,14 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// sum over the 64 lanes of a wave (returned in every lane)
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = sum16(v);
+  v += __uint_as_float(lane_xor<16>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<32>(__float_as_uint(v)));
+  return v;
+}
+
 __device__ __forceinline__ int n_valid_blocks(int seq_len, int page_size, int n_pad) {
   long long s = seq_len < 0 ? 0 : seq_len;
   long long nv = (s + page_size - 1) / page_size;

@@ -73,7 +73,14 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, int N, int K, int S, int L,
     uint32_t* tickets, float* cand_score, int32_t* cand_id, int cstride) {
-  __shared__ SelectSmem<kTopkNT, kTopkSlots> sm;
+  // the segment selects use 8 key slots; an index-order merge of at most 8192
+  // candidates uses 2 (one register tile, with the candidate ids loaded beside
+  // the scores)
+  __shared__ union {
+    SelectSmem<kTopkNT, kTopkSlots> s8;
+    SelectSmem<kTopkNT, 2> s2;
+  } smu;
+  SelectSmem<kTopkNT, kTopkSlots>& sm = smu.s8;
   __shared__ int s_last;
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x / S;
@@ -101,9 +108,13 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
   if (threadIdx.x == 0)
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  select_row<kTopkNT, kTopkSlots, SORTED, true, false>(
-      rs, S * K, cstride, K, MappedIdsOut{ids + (size_t)b * K, ri}, counts ? counts + b : nullptr,
-      sm, sort_lds);
+  const MappedIdsOut out{ids + (size_t)b * K, ri};
+  if (!SORTED && S * K <= kTopkNT * 2 * 4)  // (score order reads ids by index: no payload)
+    select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true>(
+        rs, S * K, cstride, K, out, counts ? counts + b : nullptr, smu.s2, sort_lds);
+  else
+    select_row<kTopkNT, kTopkSlots, SORTED, true, false, MappedIdsOut, true>(
+        rs, S * K, cstride, K, out, counts ? counts + b : nullptr, sm, sort_lds);
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------

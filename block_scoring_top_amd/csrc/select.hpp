@@ -61,6 +61,9 @@ struct SelectSmem {
   alignas(16) uint32_t hist[2][kBins];
   uint32_t wpack[NW];  // per-wave counts of the blocked emit
   uint32_t wmin[NW], wmax[NW];  // per-wave min / max of the keys in play
+  float wsum[NW];               // per-wave sums and counts of the scored entries
+  uint32_t wcnt[NW];            // (the mapping choice of the 8-slot linear pass)
+  uint32_t bin_max;             // max key of the linear threshold bin
   uint32_t sel_bin, sel_need, sel_tot, n_cand, all_same, same_key;
   uint32_t n_gather, gather[kWave];  // the keys of a small threshold bin
   uint32_t wtot[NW];                 // per-wave bin totals of the bin search
@@ -132,6 +135,43 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int cap, int 
     for (int j = 0; j < 4; ++j) {
       const int e = base + (i * NT + t) * 4 + j;
       keys[i][j] = e < n ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+    }
+  }
+}
+
+// Loads the entries of `src` (written by other workgroups: agent-scope loads)
+// at the places load_keys reads the keys of the same tile, as raw bits; entries
+// past n are not read (their lanes are never emitted).
+template <int NT, int SLOTS>
+__device__ __forceinline__ void load_payload(const int32_t* src, int n, int cap, int base,
+                                             uint32_t (&pay)[SLOTS][4]) {
+  const int t = threadIdx.x;
+  const bool aligned4 = (((uintptr_t)src & 15) == 0) && (cap & 3) == 0;
+  if (aligned4) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(src), (short)0, cap * 4, kBufferDword3);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (base + i * NT * 4 < n) {
+        const int e0 = base + (i * NT + t) * 4;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, e0 * 4, 0, kCachePolicySc1);
+        pay[i][0] = v[0];
+        pay[i][1] = v[1];
+        pay[i][2] = v[2];
+        pay[i][3] = v[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (base + i * NT * 4 < n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = base + (i * NT + t) * 4 + j;
+          pay[i][j] = (uint32_t)__hip_atomic_load(const_cast<int32_t*>(src) + (e < n ? e : 0),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
   }
 }
@@ -361,6 +401,7 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int P, uint64_t* 
 // IdsOut: the ids themselves, -1 in unused slots.
 struct IdsOut {
   static constexpr bool kUsesKey = false;  // put() ignores its key argument
+  static constexpr bool kPayload = false;
   int32_t* ids;
   __device__ __forceinline__ void put(int pos, int id, uint32_t) const { ids[pos] = id; }
   __device__ __forceinline__ void pad(int k) const { ids[k] = -1; }
@@ -376,6 +417,7 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
 // unused slots hold -inf (never selected).
 struct CandOut {
   static constexpr bool kUsesKey = true;  // the score is written beside the id
+  static constexpr bool kPayload = false;
   float* score;
   int32_t* id;
   int base;  // the segment's first index in the row
@@ -390,14 +432,19 @@ struct CandOut {
 };
 
 // MappedIdsOut: selecting over a candidate list, the id of candidate i is
-// map[i] (written by other workgroups: read with agent-scope loads).
+// map[i] (written by other workgroups: read with agent-scope loads). Striped
+// rows of 1 or 2 key slots load the map beside the keys (kPayload), in the same layout, so the
+// index-order emit writes each id from a register (put_payload); the score
+// order looks ids up (put).
 struct MappedIdsOut {
   static constexpr bool kUsesKey = false;
+  static constexpr bool kPayload = true;
   int32_t* ids;
   const int32_t* map;
   __device__ __forceinline__ void put(int pos, int i, uint32_t) const {
     ids[pos] = __hip_atomic_load(map + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __device__ __forceinline__ void put_payload(int pos, uint32_t v) const { ids[pos] = (int32_t)v; }
   __device__ __forceinline__ void pad(int k) const { ids[k] = -1; }
 };
 
@@ -425,11 +472,20 @@ __device__ __forceinline__ void sort_pairs_desc(uint64_t* sortbuf, int m, int P,
 
 // The linear bin of a key: the same float arithmetic as the linear pass (the
 // key's score, scaled and shifted, clamped to [0, kBins - 1]).
+// Value bins: x = score * scale + off (one fma). Key bins: x = (key - klo) *
+// scale in the order-key domain, whose spacing grows with the magnitude
+// (sign, exponent, mantissa), for rows of one sign that span many octaves.
+// Both are monotone in the key and clamp to [0, kBins - 1].
 struct BinMap {
   float scale, off;
-  __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
-    const float x = __builtin_fmaf(key_to_score(key), scale, off);
+  uint32_t klo;
+  bool by_key;
+  __device__ __forceinline__ uint32_t bin(uint32_t key, float score) const {
+    const float x = by_key ? (float)(key - klo) * scale : __builtin_fmaf(score, scale, off);
     return (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1));
+  }
+  __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
+    return bin(key, key_to_score(key));
   }
 };
 
@@ -538,8 +594,10 @@ __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uin
 
 // BLOCKED: the caller guarantees n <= NT * SLOTS * 4; the row is held in the
 // blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
-// when it does not fit one register tile).
-template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut>
+// when it does not fit one register tile). ADAPTIVE: the linear pass of a
+// striped row chooses value or key bins from the mean of its scores.
+template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut,
+          bool ADAPTIVE = (!BLOCKED && SLOTS >= 8)>
 __device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
                                                          const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
@@ -561,12 +619,16 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     return BLOCKED ? 4 * i < kpt4 : base + i * NT * 4 < n;
   };
 
+  constexpr bool kPay = Out::kPayload && !BLOCKED && SLOTS <= 2;  // (registers: 4 per slot)
   uint32_t keys[SLOTS][4];
   uint32_t raw[BLOCKED ? SLOTS : 1][4];  // blocked rows: the scores' bits as loaded
-  if constexpr (BLOCKED)
+  uint32_t pay[kPay ? SLOTS : 1][4];     // striped rows with a payload: out.map's entries
+  if constexpr (BLOCKED) {
     load_keys_blocked<NT, SLOTS, COHERENT>(row, n, cap, kpt4, keys, raw);
-  else if (cached)
+  } else if (cached) {
     load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
+    if constexpr (kPay) load_payload<NT, SLOTS>(out.map, n, cap, 0, pay);
+  }
 
   // The linear bins and the all-equal exits need the min and max of the keys
   // in play: after the first pass those of the row (rows that try the linear
@@ -578,14 +640,19 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   // rows of the fused select (dot-product scores) skip that second range: its
   // cost on every row outweighs the pass it saves on tied rows, and the third
   // pass resolves every remaining bit either way.
-  // Rows held in registers first try one pass over linear value bins (below),
-  // except in the 8-slot instances (few long idx_topk rows, any distribution):
-  // on quantised or tied rows the wasted pass costs more (measured: 30.5 ->
-  // 40 us on the top-K stress rows) than it saves on spread-out ones.
-  constexpr bool kLinear = BLOCKED || SLOTS <= 2;
+  // Rows held in registers first try one pass over linear bins (below): the
+  // blocked and the 1- and 2-slot instances, and the 8-slot instances (few
+  // long idx_topk rows, any distribution), which choose the bins per row from
+  // the mean of the scores (kAdaptive). Not the 4-slot striped instances
+  // (rows longer than one tile of the fused select, held in registers only
+  // when a request is shorter than its table).
+  constexpr bool kAdaptive = ADAPTIVE && !BLOCKED;
+  constexpr bool kLinear = BLOCKED || SLOTS <= 2 || kAdaptive;
   const bool upfront = kLinear && cached;  // the range is taken before the passes
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   if (upfront) {
+    float fsum = 0.f;
+    uint32_t fcnt = 0u;
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       if (!slot_live(0, i)) continue;
@@ -594,13 +661,26 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         const uint32_t key = keys[i][j];
         kmin = min(kmin, key == kKeyNegInf ? 0xFFFFFFFFu : key);
         kmax = max(kmax, key);
+        if constexpr (kAdaptive) {
+          const bool act = key != kKeyNegInf;
+          fsum += act ? key_to_score(key) : 0.f;
+          fcnt += act ? 1u : 0u;
+        }
       }
     }
     kmin = wave_reduce_minmax<true>(kmin);
     kmax = wave_reduce_minmax<false>(kmax);
+    if constexpr (kAdaptive) {
+      fsum = wave_sum_f32(fsum);
+      fcnt = readlane<uint32_t>(wave_incl_scan(fcnt), kWave - 1);
+    }
     if (lane == 0) {
       sm.wmin[w] = kmin;
       sm.wmax[w] = kmax;
+      if constexpr (kAdaptive) {
+        sm.wsum[w] = fsum;
+        sm.wcnt[w] = fcnt;
+      }
     }
   }
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
@@ -619,7 +699,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   // higher bins, histogram 0 per-bin counters
   bool by_bins = false;
   uint32_t bins[SLOTS][4];
-  float bin_scale = 0.f, bin_off = 0.f;  // a key's bin: fmed3(fma(score, scale, off), 0, kBins - 1)
+  BinMap bin_map{0.f, 0.f, 0u, false};  // the linear pass's bins
 
   // The linear pass: with the row's range [lo, hi], key x goes to bin
   // floor((x - lo) * kBins / (hi - lo)), clamped to the last bin (monotone in
@@ -639,12 +719,26 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     const float flo = key_to_score(lo), fhi = key_to_score(hi);
     const float span = fhi - flo;
     const float scale = (float)kBins / span;
-    // the same values in every wave: the branch is uniform over the workgroup
-    if (lo < hi && __builtin_isfinite(flo) && __builtin_isfinite(fhi) &&
-        __builtin_isfinite(span) && span > 0.f && __builtin_isfinite(scale)) {
-      const float off = -flo * scale;
-      bin_scale = scale;
-      bin_off = off;
+    // the same values in every wave: the branches are uniform over the workgroup
+    const bool value_ok = lo < hi && __builtin_isfinite(flo) && __builtin_isfinite(fhi) &&
+                          __builtin_isfinite(span) && span > 0.f && __builtin_isfinite(scale);
+    bool by_key = false;
+    if constexpr (kAdaptive) {
+      // Rows of one sign whose mean sits in the outer 1/32 of [lo, hi]
+      // (heavy-tailed rows: most scores crowd one end, where value bins would
+      // put the K-th score in a bin of hundreds) take key bins.
+      float fs = lane < NW ? sm.wsum[lane] : 0.f;
+      uint32_t fc = lane < NW ? sm.wcnt[lane] : 0u;
+      fs = wave_sum_f32(fs);
+      fc = readlane<uint32_t>(wave_incl_scan(fc), kWave - 1);
+      const float pos = (fs / (float)fc - flo) / span;  // NaN or inf when degenerate
+      const bool one_sign = lo >= 0x80000000u || hi < 0x80000000u;
+      by_key = lo < hi && one_sign && !(pos >= 1.f / 32.f && pos <= 31.f / 32.f);
+    }
+    if (value_ok || by_key) {
+      const BinMap bm{by_key ? (float)kBins / (float)(hi - lo) : scale, by_key ? 0.f : -flo * scale,
+                      lo, by_key};
+      bin_map = bm;
       uint32_t* h = sm.hist[0];
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
@@ -659,8 +753,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
             f = __uint_as_float(raw[i][j]);
           else
             f = key_to_score(keys[i][j]);
-          const float x = __builtin_fmaf(f, scale, off);
-          const uint32_t bin = act ? (uint32_t)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1)) : 0u;
+          const uint32_t bin = act ? bm.bin(keys[i][j], f) : 0u;
           bins[i][j] = bin;
           // Spread-out bins rarely collide within a wave, so lanes add their
           // own counts; a wave whose active lanes all share lane 0's bin
@@ -681,6 +774,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       if (t == 0) {
         sm.n_gather = 0u;
         sm.same_key = 0xFFFFFFFFu;
+        sm.bin_max = 0u;
       }
       __syncthreads();
       if constexpr (SORTED)
@@ -771,9 +865,36 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           by_bins = SORTED;
         }
       } else {
-        // the linear counts are in histogram 0 and histogram 1 is clear, or
-        // (score-ordered rows) histogram 0 was zeroed for counters
-        boff = SORTED ? 0 : 1;
+        // too many to gather: when every key of the bin is the same
+        // (quantised or tied rows), that key is the threshold
+        uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+          if (!slot_live(0, i)) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool g = keys[i][j] != kKeyNegInf && bins[i][j] == sb;
+            bmin = g ? min(bmin, keys[i][j]) : bmin;
+            bmax = g ? max(bmax, keys[i][j]) : bmax;
+          }
+        }
+        bmin = wave_reduce_minmax<true>(bmin);
+        bmax = wave_reduce_minmax<false>(bmax);
+        if (lane == 0 && bmin <= bmax) {
+          atomicMin(&sm.same_key, bmin);
+          atomicMax(&sm.bin_max, bmax);
+        }
+        __syncthreads();
+        if (sm.same_key == sm.bin_max) {
+          prefix = sm.same_key;
+          need = bneed;
+          level = kPasses;
+          resolved = true;
+        } else {
+          // the linear counts are in histogram 0 and histogram 1 is clear, or
+          // (score-ordered rows) histogram 0 was zeroed for counters
+          boff = SORTED ? 0 : 1;
+        }
       }
     }
   }
@@ -986,6 +1107,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     if (!cached) {
       __syncthreads();  // the previous tile's counts have been read
       load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
+      if constexpr (kPay) load_payload<NT, SLOTS>(out.map, n, cap, tile * TILE, pay);
     }
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
@@ -1030,6 +1152,8 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           const int id = tbase + (i * NT + t) * 4 + j;
           if constexpr (SORTED) {
             sortbuf[pos] = (uint64_t)keys[i][j] << 32 | (uint32_t)~id;
+          } else if constexpr (kPay) {
+            out.put_payload((int)pos, pay[i][j]);
           } else {
             out.put((int)pos, id, keys[i][j]);
           }
@@ -1052,13 +1176,12 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     // P <= 4 * NT: callers give 256- and 512-thread workgroups at most 1024 ids
     // to order (1024-thread ones take up to kMaxSortedK = 4 * 1024)
     if (by_bins) {
-      const BinMap bm{bin_scale, bin_off};
       if (P <= NT) {
-        rank_in_bins<NT, 1>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+        rank_in_bins<NT, 1>(sortbuf, (int)m_out, bin_map, sm.hist[0], sm.hist[1], out);
       } else if (P == 2 * NT) {
-        rank_in_bins<NT, 2>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+        rank_in_bins<NT, 2>(sortbuf, (int)m_out, bin_map, sm.hist[0], sm.hist[1], out);
       } else {
-        rank_in_bins<NT, 4>(sortbuf, (int)m_out, bm, sm.hist[0], sm.hist[1], out);
+        rank_in_bins<NT, 4>(sortbuf, (int)m_out, bin_map, sm.hist[0], sm.hist[1], out);
       }
     } else {
       // zero (below every key) pads the sort up to a power of two

@@ -1,0 +1,64 @@
+"""GPU parity of idx_topk on rows shaped for the linear first pass of the
+long-row instances (1024 threads, 8 key slots). That pass takes bins linear in
+the score for rows whose mean lies inside their range, bins linear in the
+order key for rows of one sign whose mean crowds one end (heavy tails), and
+settles a threshold bin too large to gather from its min and max when all its
+keys are equal. Rows of 8000 entries run in one workgroup per row; rows of
+20000 are cut into segments whose candidates the last workgroup merges.
+
+Ids are checked bit-exactly against the oracle's selection (ties to the lower
+index), in index order or in score order.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from tests.helpers import check_ids_exact, to_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scoring_top_amd as idx  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def heavy_rows(rng, n):
+    """One row per case, float32."""
+    lognormal = rng.lognormal(0.0, 2.0, n)
+    zipf = rng.zipf(1.1, n).astype(np.float64)
+    with_inf = rng.lognormal(0.0, 2.0, n)
+    with_inf[rng.choice(n, 5, replace=False)] = np.inf
+    tied = rng.integers(1, 5, n).astype(np.float64)     # four values, three huge outliers:
+    tied[rng.choice(n, 3, replace=False)] = 1e6          # key bins, the threshold bin tied
+    outlier = np.ones(n)
+    outlier[n // 3] = 1e30                               # every other score equal
+    neg_with_dead = -rng.lognormal(0.0, 2.0, n)
+    neg_with_dead[rng.choice(n, n // 4, replace=False)] = -np.inf
+    rows = [lognormal, -lognormal, zipf, -zipf, with_inf, tied, outlier,
+            rng.random(n),                               # uniform [0, 1): value bins
+            rng.random(n) * 1e-30,                       # tiny positive scores
+            neg_with_dead]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K,sorted_out", [(8000, 256, False), (8000, 2048, True),
+                                            (20000, 300, False), (20000, 2048, True),
+                                            (20000, 4096, False)])
+def test_topk_heavy_tailed_and_tied_rows(N, K, sorted_out):
+    rng = np.random.default_rng(430 + N + K)
+    s = heavy_rows(rng, N)
+    nv = np.full(s.shape[0], N, dtype=np.int64)
+    nv[1::4] = rng.integers(K // 2, N, len(nv[1::4]))
+    say(f"[topk bins] N={N} K={K} sorted={sorted_out} rows={s.shape[0]}")
+    ids, counts = idx.idx_topk(to_dev(s), K, to_dev(nv.astype(np.int32)), sorted_out)
+    torch.cuda.synchronize()
+    check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, sorted_out)
