@@ -73,9 +73,9 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, int N, int K, int S, int L,
     uint32_t* tickets, float* cand_score, int32_t* cand_id, int cstride) {
-  // the segment selects use 8 key slots; an index-order merge of at most 8192
-  // candidates uses 2 (one register tile, with the candidate ids loaded beside
-  // the scores)
+  // segments and index-order merges of at most 8192 keys use 2 key slots (one
+  // register tile; the merge loads the candidate ids beside the scores), longer
+  // ones 8
   __shared__ union {
     SelectSmem<kTopkNT, kTopkSlots> s8;
     SelectSmem<kTopkNT, 2> s2;
@@ -91,9 +91,13 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
   const int seg_n = max(0, min(lo + L, n) - lo);
   float* rs = cand_score + (size_t)b * cstride;
   int32_t* ri = cand_id + (size_t)b * cstride;
-  select_row<kTopkNT, kTopkSlots, false, false, false>(
-      scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K,
-      CandOut{rs + (size_t)seg * K, ri + (size_t)seg * K, lo}, nullptr, sm, sort_lds);
+  const CandOut cand{rs + (size_t)seg * K, ri + (size_t)seg * K, lo};
+  if (L <= kTopkNT * 2 * 4)
+    select_row<kTopkNT, 2, false, false, false, CandOut, true>(
+        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, smu.s2, sort_lds);
+  else
+    select_row<kTopkNT, kTopkSlots, false, false, false>(
+        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, sm, sort_lds);
   // hand-off: as in the fused select (agent-scope stores, all memory operations
   // of the workgroup complete, one relaxed agent-scope ticket)
   __builtin_amdgcn_s_waitcnt(0);
