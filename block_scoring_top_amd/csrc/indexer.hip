@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
 
 // ---- idx_topk ----------------------------------------------------------------------------
 // One workgroup of NT threads per row; rows longer than NT*SLOTS*4 keys are
-// streamed through the register tile.
+// streamed through the register tile. Rows of any distribution: the linear
+// pass chooses its bins per row.
 template <bool SORTED, int NT, int SLOTS>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                   const int32_t* __restrict__ n_valid,
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<NT, SLOTS, SORTED, false, false>(
+  select_row<NT, SLOTS, SORTED, false, false, IdsOut, true>(
       scores + (size_t)b * N, n, N, K, IdsOut{ids + (size_t)b * K}, counts ? counts + b : nullptr,
       sm, sort_lds);
 }
@@ -256,8 +257,9 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
   // Rows come from HBM here, so they are read in the striped layout (every load
   // fully coalesced). Many short rows (several rows per CU, each within one
   // 256-thread register tile of 2048 keys) take 256-thread workgroups, so that
-  // several selects share a CU; otherwise 1024 threads per row. 256-thread
-  // workgroups order at most 1024 ids.
+  // several selects share a CU; otherwise 1024 threads per row, in a 2-slot
+  // tile for rows of at most 8192 entries (no dead slots), else in 8 slots.
+  // 256-thread workgroups order at most 1024 ids.
   const bool narrow = B >= 512 && N <= 2048 && (!sorted || K <= 1024);
   if (narrow) {
     if (sorted)
@@ -266,6 +268,14 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
     else
       hipLaunchKernelGGL((topk_kernel<false, 256, 2>), grid, dim3(256), 0, s, scores, n_valid,
                          ids, counts, N, K);
+  } else if (N <= kTopkNT * 2 * 4) {
+    // rows within one 2-slot tile of a 1024-thread workgroup
+    if (sorted)
+      hipLaunchKernelGGL((topk_kernel<true, kTopkNT, 2>), grid, dim3(kTopkNT), sort_lds_bytes(K), s,
+                         scores, n_valid, ids, counts, N, K);
+    else
+      hipLaunchKernelGGL((topk_kernel<false, kTopkNT, 2>), grid, dim3(kTopkNT), 0, s, scores,
+                         n_valid, ids, counts, N, K);
   } else if (sorted) {
     hipLaunchKernelGGL((topk_kernel<true, kTopkNT, kTopkSlots>), grid, dim3(kTopkNT),
                        sort_lds_bytes(K), s, scores, n_valid, ids, counts, N, K);
