@@ -235,7 +235,7 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
                                      page_size, scores_out != nullptr, stream);
   if (e != 0) return IDX_ERR_HIP;
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, (int)rows, (int)stride, K,
-                                      sorted, nullptr, stream));
+                                      sorted, nullptr, stream, /*dot_scores=*/true));
 }
 
 // -|c|^2/2 per centroid, padded with -inf to a multiple of 128 (a whole number of

@@ -42,9 +42,10 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
 
 // ---- idx_topk ----------------------------------------------------------------------------
 // One workgroup of NT threads per row; rows longer than NT*SLOTS*4 keys are
-// streamed through the register tile. Rows of any distribution: the linear
-// pass chooses its bins per row.
-template <bool SORTED, int NT, int SLOTS>
+// streamed through the register tile. ADAPTIVE (rows of any distribution):
+// the linear pass chooses its bins per row; otherwise value bins (dot-product
+// scores).
+template <bool SORTED, int NT, int SLOTS, bool ADAPTIVE = true>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                   const int32_t* __restrict__ n_valid,
                                                   int32_t* __restrict__ ids,
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<NT, SLOTS, SORTED, false, false, IdsOut, true>(
+  select_row<NT, SLOTS, SORTED, false, false, IdsOut, ADAPTIVE>(
       scores + (size_t)b * N, n, N, K, IdsOut{ids + (size_t)b * K}, counts ? counts + b : nullptr,
       sm, sort_lds);
 }
@@ -234,7 +235,7 @@ int topk_segments(int B, int N, int K) {
 }
 
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
-                int B, int N, int K, bool sorted, void* split_ws, void* stream) {
+                int B, int N, int K, bool sorted, void* split_ws, void* stream, bool dot_scores) {
   const dim3 grid((unsigned)B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int S = split_ws != nullptr ? topk_segments(B, N, K) : 1;
@@ -261,21 +262,26 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
   // tile for rows of at most 8192 entries (no dead slots), else in 8 slots.
   // 256-thread workgroups order at most 1024 ids.
   const bool narrow = B >= 512 && N <= 2048 && (!sorted || K <= 1024);
+#define IDX_LAUNCH_TOPK(SO, NT_, SL_, AD)                                                  \
+  hipLaunchKernelGGL((topk_kernel<SO, NT_, SL_, AD>), grid, dim3(NT_), SO ? sort_lds_bytes(K) : 0, \
+                     s, scores, n_valid, ids, counts, N, K)
   if (narrow) {
-    if (sorted)
-      hipLaunchKernelGGL((topk_kernel<true, 256, 2>), grid, dim3(256), sort_lds_bytes(K), s,
-                         scores, n_valid, ids, counts, N, K);
-    else
-      hipLaunchKernelGGL((topk_kernel<false, 256, 2>), grid, dim3(256), 0, s, scores, n_valid,
-                         ids, counts, N, K);
+    if (sorted) {
+      if (dot_scores) IDX_LAUNCH_TOPK(true, 256, 2, false);
+      else IDX_LAUNCH_TOPK(true, 256, 2, true);
+    } else {
+      if (dot_scores) IDX_LAUNCH_TOPK(false, 256, 2, false);
+      else IDX_LAUNCH_TOPK(false, 256, 2, true);
+    }
   } else if (N <= kTopkNT * 2 * 4) {
     // rows within one 2-slot tile of a 1024-thread workgroup
-    if (sorted)
-      hipLaunchKernelGGL((topk_kernel<true, kTopkNT, 2>), grid, dim3(kTopkNT), sort_lds_bytes(K), s,
-                         scores, n_valid, ids, counts, N, K);
-    else
-      hipLaunchKernelGGL((topk_kernel<false, kTopkNT, 2>), grid, dim3(kTopkNT), 0, s, scores,
-                         n_valid, ids, counts, N, K);
+    if (sorted) {
+      if (dot_scores) IDX_LAUNCH_TOPK(true, kTopkNT, 2, false);
+      else IDX_LAUNCH_TOPK(true, kTopkNT, 2, true);
+    } else {
+      if (dot_scores) IDX_LAUNCH_TOPK(false, kTopkNT, 2, false);
+      else IDX_LAUNCH_TOPK(false, kTopkNT, 2, true);
+    }
   } else if (sorted) {
     hipLaunchKernelGGL((topk_kernel<true, kTopkNT, kTopkSlots>), grid, dim3(kTopkNT),
                        sort_lds_bytes(K), s, scores, n_valid, ids, counts, N, K);
@@ -283,6 +289,7 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
     hipLaunchKernelGGL((topk_kernel<false, kTopkNT, kTopkSlots>), grid, dim3(kTopkNT), 0, s,
                        scores, n_valid, ids, counts, N, K);
   }
+#undef IDX_LAUNCH_TOPK
   return (int)hipGetLastError();
 }
 

@@ -14,8 +14,12 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
 // split_ws: NULL (one workgroup per row), or at least topk_split_workspace_bytes
 // of zero-filled workspace (long rows are then cut into segments selected by
 // several workgroups, merged by the last one; the workspace is left zeroed).
+// dot_scores: rows of dot-product scores (value bins in the linear pass of
+// rows up to 8192 entries); otherwise rows of any distribution (bins chosen
+// per row).
 int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
-                int B, int N, int K, bool sorted, void* split_ws, void* stream);
+                int B, int N, int K, bool sorted, void* split_ws, void* stream,
+                bool dot_scores = false);
 size_t topk_split_workspace_bytes(int B, int N, int K);
 
 // indptr == nullptr: dense tables (c is [B, N_pad, 128], seq_len gives the
