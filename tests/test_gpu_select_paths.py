@@ -8,8 +8,8 @@ rows in one key slot, longer rows in four).
 
 Centroid rows are copies drawn from a small pool of distinct rows, so equal
 rows give bit-identical scores; the ids are checked bit-exactly against the
-oracle's selection on the GPU's own scores (ties to the lower id), and the
-scores against the oracle's float64 scores.
+oracle's selection on the GPU's own scores (ties to the lower id), in index
+order or in score order, and the scores against the oracle's float64 scores.
 """
 import sys
 
@@ -91,29 +91,32 @@ def test_select_ties(B, N_pad, sorted_out, distinct):
 
 @pytest.mark.parametrize("B,N_pad", SHAPES)
 @pytest.mark.parametrize("scale", [30.0, 3e4])
-def test_select_outlier(B, N_pad, scale):
+@pytest.mark.parametrize("sorted_out", [False, True])
+def test_select_outlier(B, N_pad, scale, sorted_out):
     """One block scores far above the rest: the linear bins squeeze the other
     scores into a few bins (at 3e4, every other score shares the lowest bins)."""
     x = pooled_inputs(B, N_pad, 100000, 950 + N_pad, 256, outlier=scale)
-    say(f"[select paths] outlier B={B} N_pad={N_pad} scale={scale}")
-    check(x, 256, False)
+    say(f"[select paths] outlier B={B} N_pad={N_pad} scale={scale} sorted={sorted_out}")
+    check(x, 256, sorted_out)
 
 
 @pytest.mark.parametrize("B,N_pad", SHAPES)
 @pytest.mark.parametrize("distinct", [1, 2])
-def test_select_one_or_two_values(B, N_pad, distinct):
+@pytest.mark.parametrize("sorted_out", [False, True])
+def test_select_one_or_two_values(B, N_pad, distinct, sorted_out):
     """Every block the same row (one score per request: no linear range), or two rows."""
     x = pooled_inputs(B, N_pad, distinct, 970 + distinct + N_pad, 100)
-    say(f"[select paths] {distinct} value(s) B={B} N_pad={N_pad}")
-    check(x, 100, False)
+    say(f"[select paths] {distinct} value(s) B={B} N_pad={N_pad} sorted={sorted_out}")
+    check(x, 100, sorted_out)
 
 
 @pytest.mark.parametrize("B,N_pad", SHAPES)
-def test_select_rows_within_k(B, N_pad):
+@pytest.mark.parametrize("sorted_out", [False, True])
+def test_select_rows_within_k(B, N_pad, sorted_out):
     """Requests of at most K blocks take every block; longer ones select."""
     rng = np.random.default_rng(990 + N_pad)
     seq_len = rng.integers(1, 300 * synth.PAGE_SIZE, B)
     seq_len[0] = N_pad * synth.PAGE_SIZE
     x = pooled_inputs(B, N_pad, 100000, 991 + N_pad, 256, seq_len=seq_len)
-    say(f"[select paths] rows within K B={B} N_pad={N_pad}")
-    check(x, 256, False)
+    say(f"[select paths] rows within K B={B} N_pad={N_pad} sorted={sorted_out}")
+    check(x, 256, sorted_out)
