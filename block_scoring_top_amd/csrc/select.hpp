@@ -760,13 +760,21 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
           // (clustered rows: active lanes are a prefix of the wave unless the
           // row holds -inf scores, and an inactive lane 0 has bin 0) adds them
           // with one atomic instead of 64 serialised ones.
-          const uint64_t m = ballot(act);
-          if (m != 0) {
-            const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
-            if ((ballot(bin == b0) & m) == m) {
-              if (lane == 0) atomicAdd(&h[b0], popc64(m));
-            } else if (act) {
-              atomicAdd(&h[bin], 1u);
+          if constexpr (kAdaptive && NT >= 1024) {
+            // rows of any distribution in one workgroup per CU (long top-K
+            // rows, segments, merges): groups of 16+ lanes that share a bin
+            // add with one atomic (quantised rows, a merge's few candidate
+            // values)
+            hist_add(h, act, bin);
+          } else {
+            const uint64_t m = ballot(act);
+            if (m != 0) {
+              const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
+              if ((ballot(bin == b0) & m) == m) {
+                if (lane == 0) atomicAdd(&h[b0], popc64(m));
+              } else if (act) {
+                atomicAdd(&h[bin], 1u);
+              }
             }
           }
         }
