@@ -94,12 +94,27 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
   float* rs = cand_score + (size_t)b * cstride;
   int32_t* ri = cand_id + (size_t)b * cstride;
   const CandOut cand{rs + (size_t)seg * K, ri + (size_t)seg * K, lo};
-  if (L <= kTopkNT * 2 * 4)
+  if (L <= kTopkNT * 2 * 4 && K <= kBins) {
+    // The candidates are staged in the histogram LDS, free once the
+    // threshold is known, and then written out contiguously: whole lines,
+    // where the emit's own stores would cover only its taken lanes.
+    float* st_s = reinterpret_cast<float*>(smu.s2.hist[0]);
+    int32_t* st_i = reinterpret_cast<int32_t*>(smu.s2.hist[1]);
+    select_row<kTopkNT, 2, false, false, false, StagedCandOut, true>(
+        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, StagedCandOut{st_s, st_i, lo},
+        nullptr, smu.s2, sort_lds);
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += kTopkNT) {
+      __hip_atomic_store(cand.score + k, st_s[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cand.id + k, st_i[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (L <= kTopkNT * 2 * 4) {
     select_row<kTopkNT, 2, false, false, false, CandOut, true>(
         scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, smu.s2, sort_lds);
-  else
+  } else {
     select_row<kTopkNT, kTopkSlots, false, false, false>(
         scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, sm, sort_lds);
+  }
   // hand-off: as in the fused select (agent-scope stores, all memory operations
   // of the workgroup complete, one relaxed agent-scope ticket)
   __builtin_amdgcn_s_waitcnt(0);

@@ -431,6 +431,25 @@ struct CandOut {
   }
 };
 
+// StagedCandOut: CandOut's (score, row index) pairs written to LDS arrays of K
+// entries (the caller copies them out once the select has returned); unused
+// slots hold -inf and -1. The emit must not touch the LDS they occupy.
+struct StagedCandOut {
+  static constexpr bool kUsesKey = true;
+  static constexpr bool kPayload = false;
+  float* score;
+  int32_t* id;
+  int base;  // the segment's first index in the row
+  __device__ __forceinline__ void put(int pos, int i, uint32_t key) const {
+    score[pos] = key_to_score(key);
+    id[pos] = base + i;
+  }
+  __device__ __forceinline__ void pad(int k) const {
+    score[k] = -__builtin_inff();
+    id[k] = -1;
+  }
+};
+
 // MappedIdsOut: selecting over a candidate list, the id of candidate i is
 // map[i] (written by other workgroups: read with agent-scope loads). Striped
 // rows of 1 or 2 key slots load the map beside the keys (kPayload), in the same layout, so the
