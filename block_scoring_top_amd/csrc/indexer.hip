@@ -69,8 +69,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 // segment's in ascending index order, so candidate order is index order and
 // the lower-index tie-break carries over.
 // Workspace per row: an arrival line, and cstride >= S*K candidate scores and
-// ids (cstride a multiple of 4).
-template <bool SORTED>
+// ids (cstride a multiple of 4). MS: key slots of the merge, 2 when the S*K
+// candidates fit one 2-slot tile, else 8, chosen on the host for score-ordered
+// merges (one merge per kernel keeps the registers of the 8-slot sort
+// unspilled); 0: chosen per call inside one kernel (index-order merges).
+template <bool SORTED, int MS>
 __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, int N, int K, int S, int L,
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   const MappedIdsOut out{ids + (size_t)b * K, ri};
-  if (!SORTED && S * K <= kTopkNT * 2 * 4)  // (score order reads ids by index: no payload)
+  if (MS == 2 || (MS == 0 && S * K <= kTopkNT * 2 * 4))
     select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true>(
         rs, S * K, cstride, K, out, counts ? counts + b : nullptr, smu.s2, sort_lds);
   else
@@ -262,12 +265,17 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
     float* cs = reinterpret_cast<float*>(w + topk_ticket_bytes(B));
     int32_t* ci = reinterpret_cast<int32_t*>(w + topk_ticket_bytes(B) + (size_t)B * cstride * 4);
     const dim3 g2((unsigned)((int64_t)B * S));
-    if (sorted)
-      hipLaunchKernelGGL((topk_split_kernel<true>), g2, dim3(kTopkNT), sort_lds_bytes(K), s,
-                         scores, n_valid, ids, counts, N, K, S, L, tickets, cs, ci, cstride);
-    else
-      hipLaunchKernelGGL((topk_split_kernel<false>), g2, dim3(kTopkNT), 0, s, scores, n_valid,
-                         ids, counts, N, K, S, L, tickets, cs, ci, cstride);
+    const bool merge2 = (int64_t)S * K <= kTopkNT * 2 * 4;
+#define IDX_LAUNCH_SPLIT(SO, MS)                                                            \
+  hipLaunchKernelGGL((topk_split_kernel<SO, MS>), g2, dim3(kTopkNT), SO ? sort_lds_bytes(K) : 0, \
+                     s, scores, n_valid, ids, counts, N, K, S, L, tickets, cs, ci, cstride)
+    if (sorted) {
+      if (merge2) IDX_LAUNCH_SPLIT(true, 2);
+      else IDX_LAUNCH_SPLIT(true, kTopkSlots);
+    } else {
+      IDX_LAUNCH_SPLIT(false, 0);
+    }
+#undef IDX_LAUNCH_SPLIT
     return (int)hipGetLastError();
   }
   // Rows come from HBM here, so they are read in the striped layout (every load
