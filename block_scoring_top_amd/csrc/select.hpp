@@ -774,28 +774,12 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
             f = key_to_score(keys[i][j]);
           const uint32_t bin = act ? bm.bin(keys[i][j], f) : 0u;
           bins[i][j] = bin;
-          // Spread-out bins rarely collide within a wave, so lanes add their
-          // own counts; a wave whose active lanes all share lane 0's bin
-          // (clustered rows: active lanes are a prefix of the wave unless the
-          // row holds -inf scores, and an inactive lane 0 has bin 0) adds them
-          // with one atomic instead of 64 serialised ones.
-          if constexpr (kAdaptive && NT >= 1024) {
-            // rows of any distribution in one workgroup per CU (long top-K
-            // rows, segments, merges): groups of 16+ lanes that share a bin
-            // add with one atomic (quantised rows, a merge's few candidate
-            // values)
-            hist_add(h, act, bin);
-          } else {
-            const uint64_t m = ballot(act);
-            if (m != 0) {
-              const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
-              if ((ballot(bin == b0) & m) == m) {
-                if (lane == 0) atomicAdd(&h[b0], popc64(m));
-              } else if (act) {
-                atomicAdd(&h[bin], 1u);
-              }
-            }
-          }
+          // Linear bins are spread out by construction, so every lane adds
+          // its own count: independent atomics, with no per-key wave test.
+          // Rows whose scores all share one bin except an outlier's, and
+          // quantised rows, measured the same as with merged adds of shared
+          // bins.
+          if (act) atomicAdd(&h[bin], 1u);
         }
       }
       if (t == 0) {
