@@ -826,21 +826,17 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
         resolved = true;
         by_bins = SORTED;
       } else if (btot <= (uint32_t)kWave) {
-        // gather the bin's keys: one slot reservation per wave and key slot
+        // gather the bin's keys into LDS
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
           if (!slot_live(0, i)) continue;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool g = keys[i][j] != kKeyNegInf && bins[i][j] == sb;
-            const uint64_t gm = ballot(g);
-            if (gm != 0) {
-              const int l0 = __builtin_ctzll(gm);
-              uint32_t base = 0;
-              if (lane == l0) base = atomicAdd(&sm.n_gather, popc64(gm));
-              base = readlane<uint32_t>(base, l0);
-              if (g) sm.gather[base + mbcnt(gm)] = keys[i][j];
-            }
+            // at most 64 keys of the row match: one slot per key from an LDS
+            // atomic, with no per-key wave test (the rank below does not
+            // depend on the order)
+            if (keys[i][j] != kKeyNegInf && bins[i][j] == sb)
+              sm.gather[atomicAdd(&sm.n_gather, 1u)] = keys[i][j];
           }
         }
         __syncthreads();
