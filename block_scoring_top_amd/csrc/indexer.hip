@@ -289,12 +289,13 @@ int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32
   hipLaunchKernelGGL((topk_kernel<SO, NT_, SL_, AD>), grid, dim3(NT_), SO ? sort_lds_bytes(K) : 0, \
                      s, scores, n_valid, ids, counts, N, K)
   if (narrow) {
-    // dot-product rows (the prompt-token select) in 512-thread workgroups with
-    // one key slot (prompt tokens 16.7 -> 16.4 us); rows of any distribution
-    // in 256-thread ones with two (1024 rows x 2048: 10.1 us, against 10.8 in
-    // 512-thread workgroups)
+    // index-order dot-product rows (the prompt-token select) in 512-thread
+    // workgroups with one key slot (prompt tokens 16.7 -> 16.4 us; in score
+    // order 16.8 -> 18.0 us, so those keep 256 threads); rows of any
+    // distribution in 256-thread ones with two (1024 rows x 2048: 10.1 us,
+    // against 10.8 in 512-thread workgroups)
     if (sorted) {
-      if (dot_scores) IDX_LAUNCH_TOPK(true, 512, 1, false);
+      if (dot_scores) IDX_LAUNCH_TOPK(true, 256, 2, false);
       else IDX_LAUNCH_TOPK(true, 256, 2, true);
     } else {
       if (dot_scores) IDX_LAUNCH_TOPK(false, 512, 1, false);
