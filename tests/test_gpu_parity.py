@@ -306,8 +306,11 @@ def test_topk_long_rows_split_into_segments(K, sorted_out):
     np.testing.assert_array_equal(counts2, counts)
 
 
-@pytest.mark.parametrize("N", [1, 3, 1000, 32768, 32769, 70001])
+@pytest.mark.parametrize("N", [1, 3, 1000, 8191, 8192, 32768, 32769, 70001])
 def test_topk_lengths(N):
+    """Row lengths around the layouts: one 2-slot tile (up to 8191 entries a
+    row stays whole), two segments of 4096 staged in LDS (8192), 8-slot
+    segments (32769 and longer rows), and the 2- and 8-slot merges."""
     x = synth.make_topk(9, N, 300, 401 + N)
     say(f"[topk] N={N}")
     for srt in (False, True):
