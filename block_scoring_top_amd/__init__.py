@@ -84,11 +84,24 @@ def idx_status_string(status: int) -> str:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for the c_void_p arguments
+    return None if t is None else t.data_ptr()
+
+
+# torch's raw accessor for the current stream handle costs a tenth of building
+# the Stream object (about 0.2 against 2 us a call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current stream's handle on `device` (a torch.device or an index)."""
+    if _raw_stream is not None:
+        if isinstance(device, int):
+            index = device
+        else:
+            index = device.index if device.index is not None else torch.cuda.current_device()
+        return _raw_stream(index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(t):
@@ -121,7 +134,7 @@ _ws_cache: dict = {}
 
 
 def _workspace(device, nbytes, kind):
-    key = (kind, device.index, torch.cuda.current_stream(device).cuda_stream)
+    key = (kind, device.index, _stream(device))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
