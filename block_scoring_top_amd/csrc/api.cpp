@@ -29,10 +29,12 @@ int chunk_rows(int B, int N_pad, uint32_t flags, int lo, int target) {
 // idx_score: 256-thread workgroups, 16 rows per step, ~1024 of them (4 per CU)
 constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
 // idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~256 of
-// them: one per CU, all resident at once); many requests -> 512-thread
-// workgroups (16 rows per step, ~1024)
+// them: one per CU, all resident at once; chunks of at least 32 rows, so that
+// small calls spread over more CUs: the tiny score-ordered call of 1024
+// blocks took 7.8 us with 64-row chunks, 7.55 with 32, 7.9 with 16); many
+// requests -> 512-thread workgroups (16 rows per step, ~1024)
 constexpr int kWideMaxRequests = 32;
-constexpr int kWideChunkMin = 64, kWideTarget = 256;
+constexpr int kWideChunkMin = 32, kWideTarget = 256;
 
 int check_chunk_flag(uint32_t flags) {
   const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
