@@ -13,7 +13,7 @@ import threading
 
 import torch
 
-__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
+__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
            "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
            "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
@@ -33,6 +33,8 @@ _SIGS = {
     "idx_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
     "idx_select": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _u32, _vp, _c_size, _vp]),
+    "idx_select_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _u32, _vp]),
     "idx_select_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                   _c_int, ctypes.c_int64, _c_int, _c_int, _c_int, _u32, _vp,
                                   _c_size, _vp]),
@@ -204,6 +206,28 @@ def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False
     _check("idx_select", lib.idx_select(_ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts),
                                         _ptr(scores_out), B, H, D, N_pad, page_size, K,
                                         _dtype_code(q), flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return ids, counts, scores_out
+
+
+def idx_select_noalloc(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False,
+                       ids=None, counts=None, scores_out=None, chunk_log2=0):
+    """idx_select without a workspace: the library's static per-GPU scratch holds
+    the arrival counters and staging (calls on one GPU must not overlap).
+    Returns (ids, counts, scores_out or None)."""
+    lib = load()
+    dev = _dev(q, c, seq_len, ids, counts, scores_out)
+    B, H, D = q.shape
+    N_pad = c.shape[1]
+    if ids is None:
+        ids = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    if return_scores and scores_out is None:
+        scores_out = torch.empty(B, N_pad, dtype=torch.float32, device=dev)
+    flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+    _check("idx_select_noalloc", lib.idx_select_noalloc(
+        _ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts), _ptr(scores_out), B, H, D,
+        N_pad, page_size, K, _dtype_code(q), flags, _stream(dev)))
     return ids, counts, scores_out
 
 

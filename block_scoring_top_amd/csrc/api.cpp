@@ -34,6 +34,9 @@ constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
 // blocks took 7.8 us with 64-row chunks, 7.55 with 32, 7.9 with 16); many
 // requests -> 512-thread workgroups (16 rows per step, ~1024)
 constexpr int kWideMaxRequests = 32;
+// largest score-ordered K that the many-request workgroups (512 threads) sort
+// (kept at four ids per thread of a 256-thread workgroup)
+constexpr int kNarrowMaxSortedK = 1024;
 constexpr int kWideChunkMin = 32, kWideTarget = 256;
 
 int check_chunk_flag(uint32_t flags) {
@@ -74,6 +77,7 @@ const char* idx_status_string(int status) {
     case IDX_ERR_UNSUPPORTED: return "unsupported configuration";
     case IDX_ERR_WORKSPACE: return "workspace missing or too small";
     case IDX_ERR_HIP: return "HIP launch failed";
+    case IDX_ERR_SCRATCH: return "shape exceeds the static scratch of idx_select_noalloc";
     default: return "unknown status";
   }
 }
@@ -112,19 +116,21 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
                                       need > 0 ? ws : nullptr, stream));
 }
 
-// largest score-ordered K that the many-request workgroups (512 threads) sort
-// (kept at four ids per thread of a 256-thread workgroup)
-constexpr int kNarrowMaxSortedK = 1024;
-
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {
   (void)H; (void)K; (void)flags;
   if (B < 1 || N_pad < 1) return 0;
   return kTicketBytes + (size_t)B * stage_stride(N_pad) * sizeof(float);
 }
 
-int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids, int32_t* counts,
-               float* scores_out, int B, int H, int D, int N_pad, int page_size, int K,
-               idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by idx_select and idx_select_noalloc (everything but
+// the workspace).
+int check_select_args(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                      int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
+                      int page_size, int K, idx_dtype dt, uint32_t flags) {
   int st = check_scoring_args(q, c, seq_len, B, H, D, N_pad, page_size, dt);
   if (st != IDX_OK) return st;
   if (ids == nullptr || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(scores_out, 4))
@@ -132,14 +138,18 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
   if (K < 1 || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
   if ((st = check_chunk_flag(flags)) != IDX_OK) return st;
   if (B > kMaxRequests) return IDX_ERR_UNSUPPORTED;
+  if ((flags & IDX_SORTED) != 0 && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
+  return IDX_OK;
+}
+
+// Launch shape of the fused select, then the launch: 1024-thread workgroups for
+// a few requests, 512-thread ones for many; the score order of more than 1024
+// ids is sorted by 1024-thread workgroups only.
+int dispatch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                    int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
+                    int K, idx_dtype dt, uint32_t flags, uint32_t* tickets, float* stage,
+                    void* stream) {
   const bool sorted = (flags & IDX_SORTED) != 0;
-  if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
-  const size_t need = idx_workspace_bytes(B, N_pad, H, K, flags);
-  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
-  uint32_t* tickets = static_cast<uint32_t*>(ws);
-  float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
-  // 1024-thread workgroups for a few requests, 512-thread ones for many; the
-  // score order of more than 1024 ids is sorted by 1024-thread workgroups only
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
   const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
@@ -147,6 +157,43 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
                                         page_size, K, dt == IDX_BF16, sorted, chunk, wide,
                                         tickets, stage, stage_stride(N_pad), nullptr, nullptr, 0,
                                         0, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids, int32_t* counts,
+               float* scores_out, int B, int H, int D, int N_pad, int page_size, int K,
+               idx_dtype dt, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_select_args(q, c, seq_len, ids, counts, scores_out, B, H, D, N_pad,
+                                   page_size, K, dt, flags);
+  if (st != IDX_OK) return st;
+  const size_t need = idx_workspace_bytes(B, N_pad, H, K, flags);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
+  uint32_t* tickets = static_cast<uint32_t*>(ws);
+  float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
+  return dispatch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad, page_size, K, dt,
+                         flags, tickets, stage, stream);
+}
+
+int idx_select_noalloc(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                       int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
+                       int page_size, int K, idx_dtype dt, uint32_t flags, void* stream) {
+  const int st = check_select_args(q, c, seq_len, ids, counts, scores_out, B, H, D, N_pad,
+                                   page_size, K, dt, flags);
+  if (st != IDX_OK) return st;
+  if (B > IDX_NOALLOC_MAX_REQUESTS) return IDX_ERR_SCRATCH;
+  if (scores_out == nullptr &&
+      (size_t)B * stage_stride(N_pad) * sizeof(float) > (size_t)IDX_NOALLOC_STAGE_BYTES)
+    return IDX_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (idxk::noalloc_scratch(&scratch, stream) != 0) return IDX_ERR_HIP;
+  uint32_t* tickets = static_cast<uint32_t*>(scratch);
+  float* stage =
+      reinterpret_cast<float*>(static_cast<char*>(scratch) + IDX_NOALLOC_TICKET_BYTES);
+  return dispatch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad, page_size, K, dt,
+                         flags, tickets, stage, stream);
 }
 
 int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr,

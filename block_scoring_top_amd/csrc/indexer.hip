@@ -1,6 +1,9 @@
 // Kernels of the indexer path: score, top-K, fused score + top-K.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "idx.h"
 #include "launch.h"
 #include "score.hpp"
 #include "select.hpp"
@@ -375,6 +378,46 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
 #undef IDX_LAUNCH_FUSED_NT
 #undef IDX_LAUNCH_FUSED
   return (int)hipGetLastError();
+}
+
+// ---- static scratch of idx_select_noalloc ------------------------------------------------
+// Arrival lines, then score staging. Each GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` is only a stand-in for the
+// symbol: the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[IDX_NOALLOC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** out, void* stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    // arrival lines start at zero (a fill kernel, so that the clear is also
+    // correct when the first call is captured into a graph)
+    const int words = (int)(IDX_NOALLOC_TICKET_BYTES / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(128), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return 0;
 }
 
 }  // namespace idxk

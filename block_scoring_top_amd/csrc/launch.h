@@ -32,6 +32,11 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
                   float* stage, int stage_stride, const int32_t* indptr, const int32_t* indices,
                   int64_t n_indices, int n_rows, void* stream);
 
+// The calling device's copy of the static scratch of idx_select_noalloc
+// (IDX_NOALLOC_SCRATCH_BYTES). The first call on a device looks up its address
+// and clears the arrival lines with a fill kernel on `stream`.
+int noalloc_scratch(void** scratch, void* stream);
+
 int launch_assign(const void* x, const void* c, int32_t* assign, float* best, int64_t N, int C,
                   float* cnorm, void* stream);
 

@@ -56,7 +56,9 @@ enum {
   IDX_ERR_INVALID_ARG = -1, /* null / misaligned pointer, size out of range   */
   IDX_ERR_UNSUPPORTED = -2, /* legal but not built: head_dim != 128, K > 4096 sorted */
   IDX_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
-  IDX_ERR_HIP = -4          /* the HIP runtime refused the launch              */
+  IDX_ERR_HIP = -4,         /* the HIP runtime refused the launch              */
+  IDX_ERR_SCRATCH = -5      /* idx_select_noalloc: the shape needs more than its
+                               static scratch holds                              */
 };
 
 /* flags */
@@ -144,6 +146,32 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
                int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
                int page_size, int K, idx_dtype dt, uint32_t flags, void* ws,
                size_t ws_bytes, void* stream);
+
+/*
+ * idx_select_noalloc -- idx_select with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * idx_select (the ids are identical), minus ws / ws_bytes.
+ *   Scratch: the arrival counters and the score staging live in one static
+ *   device array of IDX_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held until the
+ *   process ends: arrival lines for up to IDX_NOALLOC_MAX_REQUESTS requests,
+ *   then IDX_NOALLOC_STAGE_BYTES of staging. The first call on a device looks
+ *   up that device's copy of the array and clears its arrival lines (a fill
+ *   kernel on `stream`); every call returns them to zero.
+ *   Limits: B <= IDX_NOALLOC_MAX_REQUESTS and, when scores_out is NULL,
+ *   B * round_up(N_pad, 4) * 4 <= IDX_NOALLOC_STAGE_BYTES; beyond them the call
+ *   returns IDX_ERR_SCRATCH and enqueues nothing.
+ *   The call makes no hipMalloc / hipFree and no other allocating call.
+ *   All calls on one GPU share its array: calls that may overlap on one GPU
+ *   (other streams, or other threads) race and must not be issued.
+ */
+#define IDX_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define IDX_NOALLOC_MAX_REQUESTS 4096
+#define IDX_NOALLOC_TICKET_BYTES (IDX_NOALLOC_MAX_REQUESTS * 128u)
+#define IDX_NOALLOC_STAGE_BYTES (IDX_NOALLOC_SCRATCH_BYTES - IDX_NOALLOC_TICKET_BYTES)
+int idx_select_noalloc(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                       int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
+                       int page_size, int K, idx_dtype dt, uint32_t flags, void* stream);
 
 /*
  * idx_select_paged -- idx_select over a paged centroid pool ([CS] submission

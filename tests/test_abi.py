@@ -15,7 +15,7 @@ import block_scoring_top_amd as idx
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5
 P = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
 
 
@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_paged", "idx_select_prefill",
+    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_noalloc", "idx_select_paged",
+              "idx_select_prefill",
               "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign",
               "idx_workspace_bytes",
               "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
@@ -52,7 +53,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert idx.idx_status_string(OK) == "ok"
-    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH):
         assert idx.idx_status_string(s) not in ("ok", "unknown status")
     assert idx.idx_status_string(12345) == "unknown status"
 
@@ -137,6 +138,35 @@ def select_call(lib, **kw):
 ])
 def test_select_rejects(lib, kw, want):
     assert select_call(lib, **kw) == want
+
+
+def noalloc_call(lib, **kw):
+    a = dict(q=P, c=P, seq_len=P, ids=P, counts=None, scores_out=None, B=2, H=4, D=128,
+             N_pad=100, page_size=16, K=10, dt=1, flags=0)
+    a.update(kw)
+    return lib.idx_select_noalloc(a["q"], a["c"], a["seq_len"], a["ids"], a["counts"],
+                                  a["scores_out"], a["B"], a["H"], a["D"], a["N_pad"],
+                                  a["page_size"], a["K"], a["dt"], a["flags"], None)
+
+
+# the static scratch: 16 MiB = 4096 arrival lines of 128 B + 15.5 MiB of staging
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(ids=None), INVALID), (dict(ids=P + 1), INVALID),
+    (dict(scores_out=P + 2), INVALID), (dict(K=0), INVALID), (dict(B=0), INVALID),
+    (dict(flags=0x4), INVALID), (dict(D=256), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
+    (dict(B=16385, N_pad=4), UNSUPPORTED),
+    (dict(B=4097, N_pad=4), SCRATCH),
+    (dict(B=64, N_pad=63489), SCRATCH),      # 64 * 63492 * 4 B > 15.5 MiB of staging
+    (dict(B=4096, N_pad=1000), SCRATCH),
+])
+def test_select_noalloc_rejects(lib, kw, want):
+    assert noalloc_call(lib, **kw) == want
+
+
+def test_noalloc_scratch_limits_in_the_header():
+    src = open(os.path.join(ROOT, "include", "idx.h")).read()
+    assert "#define IDX_NOALLOC_SCRATCH_BYTES (16u << 20)" in src
+    assert "#define IDX_NOALLOC_MAX_REQUESTS 4096" in src
 
 
 def paged_call(lib, **kw):
