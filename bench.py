@@ -2,36 +2,48 @@
 """Benchmark of the indexer hot path on one MI355X.
 
 A step is one call of the hot path over one batch of synthetic input that is
-already resident in HBM. The timed steps are captured once into a HIP graph and
-replayed, so the GPU runs them back to back; the host-launched (eager) time per
-call is reported beside it. By default the workload is the variable-length decode
-batch (B=4 requests, 4 bf16 query heads, 128 dims, 8192-block padded tables,
-seq_len 4096..131072 tokens at 16 tokens per block, K=256) through the fused
-idx_select. The timed steps rotate over enough copies of the inputs (over
-512 MiB) that every step reads its centroids from HBM, not from L2 or the
-256 MiB last-level cache.
+already resident in HBM. By default one run measures the five named workloads:
 
-Prints one JSON line:
-  value         valid blocks scored + selected per second (whole job, 1 GPU)
-  ms_per_step   HIP-event time per step over the timed region
-  roofline      the dominant kernel: algorithmic bytes (or flops) per launch /
-                average launch time, against the MI355X peak
-  cpu_baseline  the CPU oracle on the host cores, on a bounded sample
-  steady_us_per_call    median / min over five replays of the timed graph
-  cold_us_per_call      32 single calls, each after a 1 GiB overwrite that evicts
-                        L2 and the last-level cache (HIP events around the call)
-  host_e2e_us_per_call  host wall clock of one call plus a stream synchronise
-  sorted_us_per_call    the score-ordered output (workloads 2-4 headline the
-                        id-ordered one)
-  floor                 an empty launch and a streaming read of the same bytes
-                        (alone, and followed by one arrival counter) on this GPU
+  1  tiny fp32 indexer: B=1, H=4, 1024 blocks, K=256, score order   (idx_select)
+  2  variable-length decode batch: B=4, H=4, bf16, N_pad=8192, K=256 (idx_select)
+  3  top-K stress: 64 rows x 30000 fp32, nine distributions, K=2048  (idx_topk)
+  4  large GQA decode batch: B=128, H=16, bf16, N_pad=2048, K=256     (idx_select)
+  5  k-means assignment: 2^20 bf16 points x 1024 centroids, D=128     (idx_assign)
+
+The headline line is workload 4, the largest single-GPU indexer batch; the
+others are reported under "workloads", each with its own roofline.
+
+How a workload is timed ("hbm_cold"):
+  - the inputs are replicated into enough copies that the bytes a call really
+    reads (its algorithmic bytes, not the padded allocation) add up to at least
+    twice the 256 MiB last-level cache between two reads of the same copy;
+  - the timed steps (step i reads copy i mod copies) are captured once into a
+    HIP graph; the graph is replayed once untimed;
+  - then a 1 GiB streaming read evicts L2 and the last-level cache (a read, so
+    that no dirty lines are left whose write-back would be charged to the call);
+  - then the graph is replayed between HIP events on the replaying stream, with
+    a synchronise on each side: every step reads its inputs from HBM, and the
+    GPU runs the steps back to back without host launch gaps;
+  - the outputs of the timed steps are then checked against the CPU oracle (the
+    cpu_baseline leg); a mismatch makes the run exit non-zero.
+
+Beside it, per workload: steady_us_per_call (the same graph replayed again
+without a flush), isolated_call_us (one call after a flush, HIP events around
+that call alone; isolated_empty_us is an empty launch timed the same way, the
+events' own overhead), host_e2e_us_per_call (host wall clock of one call plus a
+synchronise), sorted_us_per_call (score-ordered output where the headline is
+id-ordered), and floor (an empty launch, and a streaming read of the call's
+algorithmic bytes, alone and followed by one cross-workgroup arrival counter,
+timed like the call).
 
 Other modes:
-  --workload N         1..7 (1: tiny fp32, 2: default, 3: top-K stress,
-                       4: large GQA batch, 5: k-means assignment, 6: paged pool,
-                       7: prompt tokens, 8: pooled keys)
+  --workload N         one workload only (1..8; 6: paged pool, 7: prompt tokens,
+                       8: pooled keys), printed as the headline
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
-  --parse-pmc DIR      turn rocprofv3 --pmc output into a traffic summary
+  --parse-pmc DIR...   turn rocprofv3 --pmc output into a traffic summary
+  --parse-trace DIR    per-workload kernel statistics of the timed regions from a
+                       rocprofv3 --kernel-trace run of this script (the regions
+                       are bracketed by empty marker launches)
 """
 from __future__ import annotations
 
@@ -50,8 +62,14 @@ sys.path.insert(0, ROOT)
 METRIC = "blocks scored+selected/sec and µs per indexer call; % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
-ROTATE_BYTES = 512 << 20
+LLC_BYTES = 256 << 20           # MI355X last-level cache (Infinity Cache)
+ROTATE_BYTES = 2 * LLC_BYTES    # distinct bytes read between two reads of one copy
+FLUSH_BYTES = 1 << 30
 CALIB_BYTES = 1 << 30
+HEADLINE = 4
+DEFAULT_SET = (1, 2, 3, 4, 5)
+# empty launches with these workgroup counts bracket a workload's timed region
+MARK_BEGIN, MARK_END = 1000, 2000
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_split_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
@@ -83,26 +101,75 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
 # ----------------------------------------------------------------------------------------
-# workloads: device inputs, one step, algorithmic bytes
+# workloads: device inputs (copy 0, replicated later), one step, algorithmic bytes, the
+# outputs of the timed steps, and the oracle side (cpu_baseline leg only)
 # ----------------------------------------------------------------------------------------
-class Indexer:
-    def __init__(self, x, torch, idx, copies):
+class Workload:
+    unit = "blocks/s"
+    sorted_variant = False      # headline id-ordered, score order reported beside it
+    dtype = "f32"
+
+    def replicate(self, copies):
+        self.inputs += [tuple(t.clone() for t in self.inputs[0]) for _ in range(copies - 1)]
+
+    def read_src(self, i):
+        return self.inputs[i % len(self.inputs)][self.read_index]
+
+    def poison_outputs(self):
+        for t in self.out_tensors():
+            t.fill_(-1515870811)  # 0xa5a5a5a5
+
+    def timed_outputs(self):
+        return [t.cpu().numpy() for t in self.out_tensors()]
+
+    def oracle_time(self, budget_s):
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            self.oracle_call(len(times))
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times), len(times)
+
+
+class Indexer(Workload):
+    read_index = 1
+
+    def __init__(self, x, torch, idx):
         self.x, self.torch, self.idx = x, torch, idx
-        q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
-        self.inputs = [(q, c, sl)] + [(q.clone(), c.clone(), sl.clone()) for _ in range(copies - 1)]
-        dev = q.device
-        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device=dev)
-        self.counts = torch.empty(x.B, dtype=torch.int32, device=dev)
+        self.dtype = x.dtype
+        self.inputs = [(to_dev(x.q), to_dev(x.c), to_dev(x.seq_len))]
+        self.sorted_variant = not x.sorted
+        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device="cuda")
+        self.counts = torch.empty(x.B, dtype=torch.int32, device="cuda")
         nbytes = idx.idx_workspace_bytes(x.B, x.N_pad, x.H, x.K, 0)
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         # blocks holding tokens: ceil(seq_len / page_size), at most N_pad
         self.nv = [min(x.N_pad, -(-int(v) // x.page_size)) for v in x.seq_len]
         elem = 2 if x.dtype == "bf16" else 4
         self.units = int(sum(self.nv))
-        self.row_bytes = x.D * elem
         # centroid rows that hold tokens + query heads + seq_len + ids written
-        self.alg_bytes = (self.units * self.row_bytes + x.q.size * elem + 4 * x.B + 4 * x.B * x.K)
+        self.alg_bytes = self.units * x.D * elem + x.q.size * elem + 4 * x.B + 4 * x.B * x.K
         self.alg_flops = 2 * self.units * x.D  # after summing the heads once per request
 
     def step(self, i, sorted=None):
@@ -111,8 +178,17 @@ class Indexer:
                             sorted=self.x.sorted if sorted is None else sorted,
                             ids=self.ids, counts=self.counts, ws=self.ws)
 
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)][1]
+    def out_tensors(self):
+        return [self.ids, self.counts]
+
+    def gpu_scores(self):
+        """One more call that also writes the scores: the GPU's own fp32 scores
+        (the ids are not taken from it)."""
+        q, c, sl = self.inputs[0]
+        _, _, s = self.idx.idx_select(q, c, sl, self.x.K, page_size=self.x.page_size,
+                                      sorted=self.x.sorted, return_scores=True)
+        self.torch.cuda.synchronize()
+        return s.cpu().numpy()
 
     def describe(self):
         x = self.x
@@ -120,36 +196,159 @@ class Indexer:
                 "N_pad": x.N_pad, "page_size": x.page_size, "K": x.K, "sorted": x.sorted,
                 "inputs": x.dtype, "accumulate": "f32", "seq_len": [int(v) for v in x.seq_len]
                 if x.B <= 8 else f"{int(x.seq_len.min())}..{int(x.seq_len.max())}",
-                "valid_blocks": self.units, "input_copies": len(self.inputs)}
+                "valid_blocks": self.units}
 
-    def cpu_oracle(self, budget_s):
+    def oracle_call(self, i):
         import oracle
         x = self.x
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            S, _ = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
-            oracle.select(S, self.nv, x.K, x.sorted)
-            times.append(time.perf_counter() - t0)
-        med = statistics.median(times)
-        return self.units / med, f"the whole batch ({self.units} valid blocks), {len(times)} " \
-                                 f"calls, median {med * 1e3:.1f} ms per call"
+        S, _ = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+        oracle.select(S, self.nv, x.K, x.sorted)
+
+    def sample_text(self, med, n):
+        return f"the whole batch ({self.units} valid blocks), {n} calls, median " \
+               f"{med * 1e3:.1f} ms per call"
+
+    def parity(self, outs, gpu_scores):
+        """C1: the timed ids are the oracle's selection from the GPU's scores;
+        C2: those scores within rtol * A of fp64; C3: the ids against the fp64
+        selection, inside the band."""
+        import oracle
+        from tests.helpers import RTOL, check_ids_band, check_ids_exact, check_scores
+        x = self.x
+        ids, counts = outs
+        S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+        nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+        rel = check_scores(gpu_scores, S, A, RTOL[x.dtype])
+        check_ids_exact(ids, counts, gpu_scores, nv, x.K, x.sorted)
+        check_ids_band(ids, S, A, nv, x.K, RTOL[x.dtype])
+        return {"C1_ids_exact": True, "C2_max_err_over_A": rel, "C3_band": True,
+                "rows": int(x.B)}
 
 
-class Paged:
-    def __init__(self, x, torch, idx, copies):
+class Topk(Workload):
+    unit = "entries/s"
+    read_index = 0
+    sorted_variant = True
+
+    def __init__(self, x, torch, idx):
         self.x, self.torch, self.idx = x, torch, idx
-        q, c = to_dev(x.q), to_dev(x.c_pool)
-        ip, ix = to_dev(x.indptr), to_dev(x.indices)
-        self.inputs = [(q, c, ip, ix)] + [(q.clone(), c.clone(), ip.clone(), ix.clone())
-                                          for _ in range(copies - 1)]
-        dev = q.device
-        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device=dev)
-        self.counts = torch.empty(x.B, dtype=torch.int32, device=dev)
-        nbytes = idx.idx_workspace_bytes(x.B, x.max_pages, x.H, x.K, 0)
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.inputs = [(to_dev(x.scores),)]
+        B, N = x.scores.shape
+        self.ids = torch.empty(B, x.K, dtype=torch.int32, device="cuda")
+        self.counts = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.ws = torch.zeros(max(256, idx.idx_topk_workspace_bytes(B, N, x.K, 1)),
+                              dtype=torch.uint8, device="cuda")
+        self.units = B * N
+        self.alg_bytes = B * N * 4 + B * x.K * 4
+        self.alg_flops = 0
+
+    def step(self, i, sorted=None):
+        self.idx.idx_topk(self.inputs[i % len(self.inputs)][0], self.x.K, None, bool(sorted),
+                          ids=self.ids, counts=self.counts, ws=self.ws)
+
+    def out_tensors(self):
+        return [self.ids, self.counts]
+
+    def gpu_scores(self):
+        return None
+
+    def describe(self):
+        B, N = self.x.scores.shape
+        return {"workload": self.x.name, "call": "idx_topk", "rows": B, "N": N, "K": self.x.K,
+                "sorted": False, "inputs": "f32", "distributions": 9}
+
+    def oracle_call(self, i):
+        import oracle
+        oracle.select(self.x.scores, None, self.x.K, False)
+
+    def sample_text(self, med, n):
+        return f"all {self.x.scores.shape[0]} rows, {n} calls, median {med * 1e3:.1f} ms per call"
+
+    def parity(self, outs, gpu_scores):
+        """C1 directly: the input scores are the GPU's own."""
+        from tests.helpers import check_ids_exact
+        ids, counts = outs
+        check_ids_exact(ids, counts, self.x.scores, None, self.x.K, False)
+        return {"C1_ids_exact": True, "rows": int(self.x.scores.shape[0])}
+
+
+class Assign(Workload):
+    unit = "points/s"
+    read_index = 0
+    dtype = "bf16"
+    SAMPLE = 2048         # points per oracle call of the CPU baseline
+    PARITY_ROWS = 8192    # sampled points checked against the oracle
+
+    def __init__(self, x, torch, idx):
+        self.x, self.torch, self.idx = x, torch, idx
+        self.inputs = [(to_dev(x.x), to_dev(x.c))]
+        N, D = x.x.shape
+        C = x.c.shape[0]
+        self.assign = torch.empty(N, dtype=torch.int32, device="cuda")
+        self.ws = torch.zeros(idx.idx_assign_workspace_bytes(C, D), dtype=torch.uint8,
+                              device="cuda")
+        self.units = N
+        self.alg_bytes = N * D * 2 + C * D * 2 + N * 4
+        self.alg_flops = 2 * N * C * D
+
+    def step(self, i, sorted=None):
+        xd, cd = self.inputs[i % len(self.inputs)]
+        self.idx.idx_assign(xd, cd, assign=self.assign, ws=self.ws)
+
+    def out_tensors(self):
+        return [self.assign]
+
+    def gpu_scores(self):
+        return None
+
+    def describe(self):
+        N, D = self.x.x.shape
+        return {"workload": self.x.name, "call": "idx_assign", "N": N, "C": self.x.c.shape[0],
+                "D": D, "inputs": "bf16", "accumulate": "f32 (MFMA)"}
+
+    def oracle_call(self, i):
+        import oracle
+        n, N = self.SAMPLE, self.x.x.shape[0]
+        lo = (i * n) % N
+        oracle.assign(self.x.x[lo:lo + n], self.x.c)
+
+    def sample_text(self, med, n):
+        return f"{self.SAMPLE} of the {self.x.x.shape[0]} points per call, {n} calls, " \
+               f"median {med * 1e3:.1f} ms per call"
+
+    def oracle_units(self):
+        return self.SAMPLE
+
+    def parity(self, outs, gpu_scores):
+        """Every point's generating component is its nearest centroid (holds at any
+        size); sampled points against the oracle's argmax, inside the band."""
         import numpy as np
+        from tests.helpers import check_assign
+        (a,) = outs
+        np.testing.assert_array_equal(a, self.x.comp)
+        rng = np.random.default_rng(5)
+        N = self.x.x.shape[0]
+        rows = np.concatenate([np.arange(64), rng.choice(N, self.PARITY_ROWS, replace=False),
+                               np.arange(N - 64, N)])
+        off = check_assign(a, None, self.x.x, self.x.c, rows)
+        return {"components_recovered": int(N), "sampled_points": int(rows.size),
+                "differ_inside_band": int(off)}
+
+
+class Paged(Workload):
+    unit = "page slots/s"
+    read_index = 1
+
+    def __init__(self, x, torch, idx):
+        import numpy as np
+        self.x, self.torch, self.idx = x, torch, idx
+        self.dtype = x.dtype
+        self.inputs = [(to_dev(x.q), to_dev(x.c_pool), to_dev(x.indptr), to_dev(x.indices))]
+        self.sorted_variant = not x.sorted
+        self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device="cuda")
+        self.counts = torch.empty(x.B, dtype=torch.int32, device="cuda")
+        nbytes = idx.idx_workspace_bytes(x.B, x.max_pages, x.H, x.K, 0)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         n = np.minimum(np.diff(x.indptr.astype(np.int64)), x.max_pages)
         self.nv = [int(v) for v in n]
         self.units = int(n.sum())                      # page slots scored
@@ -167,42 +366,59 @@ class Paged:
                                   sorted=self.x.sorted if sorted is None else sorted,
                                   ids=self.ids, counts=self.counts, ws=self.ws)
 
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)][1]
+    def out_tensors(self):
+        return [self.ids, self.counts]
+
+    def gpu_scores(self):
+        q, c, ip, ix = self.inputs[0]
+        _, _, s = self.idx.idx_select_paged(q, c, ip, ix, self.x.K, self.x.max_pages,
+                                            sorted=self.x.sorted, return_scores=True)
+        self.torch.cuda.synchronize()
+        return s.cpu().numpy()
 
     def describe(self):
         x = self.x
         return {"workload": x.name, "call": "idx_select_paged", "B": x.B, "H": x.H, "D": 128,
                 "pool_rows": int(x.c_pool.shape[0]), "max_pages": x.max_pages,
                 "page_slots": self.units, "K": x.K, "sorted": x.sorted, "inputs": x.dtype,
-                "accumulate": "f32", "input_copies": len(self.inputs)}
+                "accumulate": "f32"}
 
-    def cpu_oracle(self, budget_s):
+    def oracle_call(self, i):
         import oracle
         x = self.x
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            S, _, n = oracle.score_paged(x.q, x.c_pool, x.indptr, x.indices, x.max_pages, x.dtype)
-            oracle.select(S, n, x.K, x.sorted)
-            times.append(time.perf_counter() - t0)
-        med = statistics.median(times)
-        return self.units / med, f"the whole batch ({self.units} page slots), {len(times)} " \
-                                 f"calls, median {med * 1e3:.1f} ms per call"
+        S, _, n = oracle.score_paged(x.q, x.c_pool, x.indptr, x.indices, x.max_pages, x.dtype)
+        oracle.select(S, n, x.K, x.sorted)
+
+    def sample_text(self, med, n):
+        return f"the whole batch ({self.units} page slots), {n} calls, median " \
+               f"{med * 1e3:.1f} ms per call"
+
+    def parity(self, outs, gpu_scores):
+        import oracle
+        from tests.helpers import RTOL, check_ids_band, check_ids_exact, check_scores
+        x = self.x
+        ids, counts = outs
+        S, A, n = oracle.score_paged(x.q, x.c_pool, x.indptr, x.indices, x.max_pages, x.dtype)
+        rel = check_scores(gpu_scores, S, A, RTOL[x.dtype])
+        check_ids_exact(ids, counts, gpu_scores, n, x.K, x.sorted)
+        check_ids_band(ids, S, A, n, x.K, RTOL[x.dtype])
+        return {"C1_ids_exact": True, "C2_max_err_over_A": rel, "C3_band": True}
 
 
-class Prefill:
-    def __init__(self, x, torch, idx, copies):
-        self.x, self.torch, self.idx = x, torch, idx
-        q, c, p0 = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
-        self.inputs = [(q, c, p0)] + [(q.clone(), c.clone(), p0.clone()) for _ in range(copies - 1)]
-        dev = q.device
-        self.ids = torch.empty(x.B, x.T, x.K, dtype=torch.int32, device=dev)
-        self.counts = torch.empty(x.B, x.T, dtype=torch.int32, device=dev)
-        self.ws = torch.empty(idx.idx_prefill_workspace_bytes(x.B, x.T, x.N_pad, x.K, 0),
-                              dtype=torch.uint8, device=dev)
+class Prefill(Workload):
+    unit = "token-block pairs/s"
+    read_index = 1
+
+    def __init__(self, x, torch, idx):
         import numpy as np
+        self.x, self.torch, self.idx = x, torch, idx
+        self.dtype = x.dtype
+        self.inputs = [(to_dev(x.q), to_dev(x.c), to_dev(x.pos0))]
+        self.sorted_variant = not x.sorted
+        self.ids = torch.empty(x.B, x.T, x.K, dtype=torch.int32, device="cuda")
+        self.counts = torch.empty(x.B, x.T, dtype=torch.int32, device="cuda")
+        self.ws = torch.empty(idx.idx_prefill_workspace_bytes(x.B, x.T, x.N_pad, x.K, 0),
+                              dtype=torch.uint8, device="cuda")
         ps = x.page_size
         nv = [np.minimum(x.N_pad, (max(int(p), 0) + np.arange(x.T) + 1 + ps - 1) // ps)
               for p in x.pos0]
@@ -219,43 +435,63 @@ class Prefill:
                                     sorted=self.x.sorted if sorted is None else sorted,
                                     ids=self.ids, counts=self.counts, ws=self.ws)
 
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)][1]
+    def out_tensors(self):
+        return [self.ids, self.counts]
+
+    def gpu_scores(self):
+        q, c, p0 = self.inputs[0]
+        _, _, s = self.idx.idx_select_prefill(q, c, p0, self.x.K, page_size=self.x.page_size,
+                                              sorted=self.x.sorted, return_scores=True)
+        self.torch.cuda.synchronize()
+        return s.cpu().numpy()
 
     def describe(self):
         x = self.x
         return {"workload": x.name, "call": "idx_select_prefill", "B": x.B, "T": x.T, "H": x.H,
                 "D": 128, "N_pad": x.N_pad, "pos0": [int(v) for v in x.pos0],
                 "page_size": x.page_size, "K": x.K, "sorted": x.sorted, "inputs": x.dtype,
-                "accumulate": "f32 (MFMA)", "token_block_pairs": self.units,
-                "input_copies": len(self.inputs)}
+                "accumulate": "f32 (MFMA)", "token_block_pairs": self.units}
 
-    def cpu_oracle(self, budget_s):
+    def oracle_call(self, i):
         import oracle
         x = self.x
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            S, _, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
-            R = x.B * x.T
-            oracle.select(S.reshape(R, -1), NV.reshape(R), x.K, x.sorted)
-            times.append(time.perf_counter() - t0)
-        med = statistics.median(times)
-        return self.units / med, f"the whole batch ({self.units} token-block pairs), " \
-                                 f"{len(times)} calls, median {med * 1e3:.1f} ms per call"
+        S, _, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+        R = x.B * x.T
+        oracle.select(S.reshape(R, -1), NV.reshape(R), x.K, x.sorted)
+
+    def sample_text(self, med, n):
+        return f"the whole batch ({self.units} token-block pairs), {n} calls, median " \
+               f"{med * 1e3:.1f} ms per call"
+
+    def parity(self, outs, gpu_scores):
+        import oracle
+        from tests.helpers import RTOL, check_ids_band, check_ids_exact, check_scores
+        x = self.x
+        ids, counts = outs
+        R = x.B * x.T
+        S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+        s = gpu_scores.reshape(R, -1)
+        rel = check_scores(s, S.reshape(R, -1), A.reshape(R, -1), RTOL[x.dtype])
+        check_ids_exact(ids.reshape(R, -1), counts.reshape(R), s, NV.reshape(R), x.K, x.sorted)
+        check_ids_band(ids.reshape(R, -1), S.reshape(R, -1), A.reshape(R, -1), NV.reshape(R),
+                       x.K, RTOL[x.dtype])
+        return {"C1_ids_exact": True, "C2_max_err_over_A": rel, "C3_band": True}
 
 
-class Pool:
-    def __init__(self, x, torch, idx, copies):
-        self.x, self.torch, self.idx = x, torch, idx
-        k, sl = to_dev(x.k), to_dev(x.seq_len)
-        self.inputs = [(k, sl)] + [(k.clone(), sl.clone()) for _ in range(copies - 1)]
-        self.c = torch.zeros(x.B, x.N_pad, 128, dtype=k.dtype, device=k.device)
+class Pool(Workload):
+    unit = "blocks pooled/s"
+    read_index = 0
+
+    def __init__(self, x, torch, idx):
         import numpy as np
+        self.x, self.torch, self.idx = x, torch, idx
+        self.dtype = x.dtype
+        self.inputs = [(to_dev(x.k), to_dev(x.seq_len))]
+        self.c = torch.zeros(x.B, x.N_pad, 128, dtype=self.inputs[0][0].dtype, device="cuda")
         S_pad = x.k.shape[1]
         sl_np = np.clip(x.seq_len.astype(np.int64), 0, S_pad)
         nv = np.minimum(x.N_pad, (sl_np + x.page_size - 1) // x.page_size)
+        self.nv = nv
         tokens = int(np.minimum(sl_np, nv * x.page_size).sum())
         elem = 2 if x.dtype == "bf16" else 4
         self.units = int(nv.sum())                               # blocks pooled
@@ -267,232 +503,134 @@ class Pool:
         k, sl = self.inputs[i % len(self.inputs)]
         self.idx.idx_pool_keys(k, sl, self.x.N_pad, self.x.page_size, c=self.c)
 
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)][0]
+    def out_tensors(self):
+        return []
+
+    def poison_outputs(self):
+        self.c.fill_(float("nan"))
+
+    def timed_outputs(self):
+        import numpy as np
+        return [self.c.view(self.torch.int16).cpu().numpy().view(np.uint16)]
+
+    def gpu_scores(self):
+        return None
 
     def describe(self):
         x = self.x
         return {"workload": x.name, "call": "idx_pool_keys", "B": x.B, "S_pad": int(x.k.shape[1]),
                 "D": 128, "N_pad": x.N_pad, "page_size": x.page_size, "inputs": x.dtype,
-                "seq_len": [int(v) for v in x.seq_len], "blocks": self.units,
-                "input_copies": len(self.inputs)}
+                "seq_len": [int(v) for v in x.seq_len], "blocks": self.units}
 
-    def cpu_oracle(self, budget_s):
+    def oracle_call(self, i):
         import oracle
-        x = self.x
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            oracle.pool_keys(x.k, x.seq_len, x.N_pad, x.page_size, x.dtype)
-            times.append(time.perf_counter() - t0)
-        med = statistics.median(times)
-        return self.units / med, f"the whole batch ({self.units} blocks), {len(times)} calls, " \
-                                 f"median {med * 1e3:.1f} ms per call"
+        oracle.pool_keys(self.x.k, self.x.seq_len, self.x.N_pad, self.x.page_size, self.x.dtype)
 
+    def sample_text(self, med, n):
+        return f"the whole batch ({self.units} blocks), {n} calls, median {med * 1e3:.1f} ms " \
+               "per call"
 
-class Topk:
-    def __init__(self, x, torch, idx, copies):
-        self.x, self.torch, self.idx = x, torch, idx
-        s = to_dev(x.scores)
-        self.inputs = [s] + [s.clone() for _ in range(copies - 1)]
-        B, N = x.scores.shape
-        self.ids = torch.empty(B, x.K, dtype=torch.int32, device=s.device)
-        self.counts = torch.empty(B, dtype=torch.int32, device=s.device)
-        self.units = B * N
-        self.alg_bytes = B * N * 4 + B * x.K * 4
-        self.alg_flops = 0
-
-    def step(self, i, sorted=None):
-        self.idx.idx_topk(self.inputs[i % len(self.inputs)], self.x.K, None, bool(sorted),
-                          ids=self.ids, counts=self.counts)
-
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)]
-
-    def describe(self):
-        B, N = self.x.scores.shape
-        return {"workload": self.x.name, "call": "idx_topk", "rows": B, "N": N, "K": self.x.K,
-                "sorted": False, "inputs": "f32", "distributions": 9,
-                "input_copies": len(self.inputs)}
-
-    def cpu_oracle(self, budget_s):
-        import oracle
-        x = self.x
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            oracle.select(x.scores, None, x.K, False)
-            times.append(time.perf_counter() - t0)
-        med = statistics.median(times)
-        return self.units / med, f"all {x.scores.shape[0]} rows, {len(times)} calls, " \
-                                 f"median {med * 1e3:.1f} ms per call"
-
-
-class Assign:
-    def __init__(self, x, torch, idx, copies):
-        self.x, self.torch, self.idx = x, torch, idx
-        xd, cd = to_dev(x.x), to_dev(x.c)
-        self.inputs = [(xd, cd)] + [(xd.clone(), cd.clone()) for _ in range(copies - 1)]
-        N, D = x.x.shape
-        C = x.c.shape[0]
-        self.assign = torch.empty(N, dtype=torch.int32, device=xd.device)
-        self.ws = torch.zeros(idx.idx_assign_workspace_bytes(C, D), dtype=torch.uint8,
-                              device=xd.device)
-        self.units = N
-        self.alg_bytes = N * D * 2 + C * D * 2 + N * 4
-        self.alg_flops = 2 * N * C * D
-
-    def step(self, i, sorted=None):
-        xd, cd = self.inputs[i % len(self.inputs)]
-        self.idx.idx_assign(xd, cd, assign=self.assign, ws=self.ws)
-
-    def read_src(self, i):
-        return self.inputs[i % len(self.inputs)][0]
-
-    def describe(self):
-        N, D = self.x.x.shape
-        return {"workload": self.x.name, "call": "idx_assign", "N": N, "C": self.x.c.shape[0],
-                "D": D, "inputs": "bf16", "accumulate": "f32 (MFMA)",
-                "input_copies": len(self.inputs)}
-
-    def cpu_oracle(self, budget_s):
+    def parity(self, outs, gpu_scores):
+        """Every pooled value within the fp32-sum bound plus the bf16 output
+        rounding of the fp64 mean."""
         import numpy as np
         import oracle
-        x = self.x
-        n = 2048
-        times = []
-        t_end = time.perf_counter() + budget_s
-        i = 0
-        while time.perf_counter() < t_end or len(times) < 3:
-            rows = slice((i * n) % x.x.shape[0], (i * n) % x.x.shape[0] + n)
-            t0 = time.perf_counter()
-            oracle.assign(x.x[rows], x.c)
-            times.append(time.perf_counter() - t0)
-            i += 1
-        med = statistics.median(times)
-        return n / med, f"{n} of the {x.x.shape[0]} points per call, {len(times)} calls, " \
-                        f"median {med * 1e3:.1f} ms per call"
+        import synth
+        (bits,) = outs
+        got = synth.bf16_bits_to_f32(bits).astype(np.float64)
+        C, M, nv = oracle.pool_keys(self.x.k, self.x.seq_len, self.x.N_pad, self.x.page_size,
+                                    self.x.dtype)
+        for b in range(self.x.B):
+            m = int(nv[b])
+            err = np.abs(got[b, :m] - C[b, :m])
+            tol = 2.0 ** -8 * np.abs(C[b, :m]) + 2.0 ** -17 * M[b, :m]
+            assert not (err > tol).any(), f"request {b}: pooled values out of tolerance"
+        return {"blocks_in_tolerance": int(self.units)}
 
 
-def make(w, torch, idx, copies):
+def make(w, torch, idx):
     import synth
     x = synth.workload(w)
-    if w in (1, 2, 4):
-        return Indexer(x, torch, idx, copies)
-    if w == 3:
-        return Topk(x, torch, idx, copies)
-    if w == 6:
-        return Paged(x, torch, idx, copies)
-    if w == 7:
-        return Prefill(x, torch, idx, copies)
-    if w == 8:
-        return Pool(x, torch, idx, copies)
-    return Assign(x, torch, idx, copies)
-
-
-def input_bytes(w, x):
-    if w in (1, 2, 4):
-        return x.q.nbytes + x.c.nbytes
-    if w == 3:
-        return x.scores.nbytes
-    if w == 6:
-        return x.q.nbytes + x.c_pool.nbytes + x.indptr.nbytes + x.indices.nbytes
-    if w == 7:
-        return x.q.nbytes + x.c.nbytes
-    if w == 8:
-        return x.k.nbytes
-    return x.x.nbytes + x.c.nbytes
-
-
-def blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
+    cls = {1: Indexer, 2: Indexer, 3: Topk, 4: Indexer, 5: Assign, 6: Paged, 7: Prefill,
+           8: Pool}[w]
+    wl = cls(x, torch, idx)
+    wl.w = w
+    return wl
 
 
 # ----------------------------------------------------------------------------------------
-# timing helpers
+# timing
 # ----------------------------------------------------------------------------------------
-def graph_time(torch, fn, steps, reps=1):
-    """Capture `steps` calls fn(i) into one HIP graph; per-call ms of each of `reps`
-    replays (HIP events on the replaying stream)."""
+class Flusher:
+    """Evicts L2 and the last-level cache with a 1 GiB streaming read (the
+    library's floor read launch: reads only, so no dirty lines are left)."""
+
+    def __init__(self, torch, idx):
+        self.torch, self.idx = torch, idx
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.idx.idx_floor_read(self.buf, FLUSH_BYTES, self.sink, None, 2048, 256)
+
+
+def capture(torch, fn, steps, warm=3):
+    """Capture `steps` calls fn(i) into one HIP graph (after a few eager calls on
+    the capturing stream, so that nothing is first touched inside the capture)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(3):
+        for i in range(warm):
             fn(i)
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
             fn(i)
-    g.replay()
+    return g
+
+
+def replay_ms(torch, g, steps, flush=None, mark=None, idx=None):
+    """Per-step ms of one replay of g, HIP events on the replaying stream, with a
+    synchronise on each side; optionally after a flush, and bracketed by marker
+    launches that a kernel trace can find."""
+    stream = torch.cuda.current_stream()
+    if flush is not None:
+        flush()
+    if mark is not None:
+        idx.idx_floor_empty(MARK_BEGIN + mark)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    out = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if mark is not None:
+        idx.idx_floor_empty(MARK_END + mark)
         torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) / steps)
-    del g
-    return out
+    return e0.elapsed_time(e1) / steps
 
 
-def floors(torch, idx, wl, steps):
-    """Attainable floor at this size: an empty launch, and a streaming read of the
-    call's algorithmic bytes (rotating over the input copies, so from HBM), alone
-    and followed by one arrival counter; the read takes the best of a small sweep
-    of launch shapes."""
-    src0 = wl.read_src(0)
-    nbytes = min(wl.alg_bytes, src0.numel() * src0.element_size()) // 16 * 16
-    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
-    ticket = torch.zeros(64, dtype=torch.int32, device="cuda")
-    res = {"bytes": nbytes,
-           "empty_us": min(graph_time(torch, lambda i: idx.idx_floor_empty(1), steps, 3)) * 1e3}
-    for key, tk in (("read", None), ("read_handoff", ticket)):
-        best = None
-        for threads in (256, 1024):
-            for blocks in (64, 128, 256, 512, 1024, 2048):
-                t = min(graph_time(torch, lambda i: idx.idx_floor_read(
-                    wl.read_src(i), nbytes, sink, tk, blocks, threads), steps, 3)) * 1e3
-                if best is None or t < best[0]:
-                    best = (t, blocks, threads)
-        res[key + "_us"] = best[0]
-        res[key + "_launch"] = f"{best[1]} x {best[2]}"
-    res["read_GBps"] = nbytes / (res["read_us"] * 1e-6) / 1e9
-    return res
-
-
-def cold_times(torch, wl, n):
-    """Per-call GPU time with L2 and the last-level cache flushed before each call
-    (a 1 GiB buffer is overwritten first)."""
-    flush = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+def isolated_ms(torch, fn, flush, n):
+    """One call after a flush, HIP events around that call alone."""
     out = []
     for i in range(n):
-        flush.fill_(float(i))
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        wl.step(i)
+        fn(i)
         e1.record()
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1))
-    del flush
     return out
 
 
-def host_e2e_times(torch, wl, n):
+def host_e2e_ms(torch, fn, n):
     """Wall clock of one host call plus a stream synchronise."""
     out = []
     for i in range(n):
         t0 = time.perf_counter()
-        wl.step(i)
+        fn(i)
         torch.cuda.synchronize()
         out.append((time.perf_counter() - t0) * 1e3)
     return out
@@ -503,8 +641,116 @@ def stats_us(ms_list):
             "n": len(ms_list)}
 
 
+def floors(torch, idx, wl, steps, flush):
+    """Attainable floor at this size, timed like the call: an empty launch, and a
+    streaming read of the call's algorithmic bytes over the same rotating copies
+    after a flush, alone and followed by one arrival counter; the read takes the
+    best of a small sweep of launch shapes."""
+    src0 = wl.read_src(0)
+    nbytes = min(wl.alg_bytes, src0.numel() * src0.element_size()) // 16 * 16
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    ticket = torch.zeros(64, dtype=torch.int32, device="cuda")
+    g = capture(torch, lambda i: idx.idx_floor_empty(1), steps)
+    g.replay()
+    res = {"bytes": nbytes, "empty_us": min(replay_ms(torch, g, steps) for _ in range(3)) * 1e3}
+    del g
+    for key, tk in (("read", None), ("read_handoff", ticket)):
+        best = None
+        for threads in (256, 1024):
+            for blocks in (128, 256, 512, 1024, 2048):
+                g = capture(torch, lambda i: idx.idx_floor_read(
+                    wl.read_src(i), nbytes, sink, tk, blocks, threads), steps)
+                g.replay()
+                t = replay_ms(torch, g, steps, flush) * 1e3
+                del g
+                if best is None or t < best[0]:
+                    best = (t, blocks, threads)
+        res[key + "_us"] = best[0]
+        res[key + "_launch"] = f"{best[1]} x {best[2]}"
+    res["read_GBps"] = nbytes / (res["read_us"] * 1e-6) / 1e9
+    return res
+
+
+def roofline(wl, ms, traffic):
+    if wl.w == 5:
+        achieved = wl.alg_flops / (ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": KERNEL[wl.w], "achieved": achieved,
+             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+             "alg_flops_per_launch": wl.alg_flops, "alg_bytes_per_launch": wl.alg_bytes,
+             "hbm_frac": wl.alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    else:
+        achieved = wl.alg_bytes / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "kernel": KERNEL[wl.w], "achieved": achieved,
+             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+             "traffic": traffic, "alg_bytes_per_launch": wl.alg_bytes}
+    return r
+
+
+def measure(torch, idx, wl, steps, warmup, extras, flush):
+    """Time one workload as the module docstring describes; returns its result
+    dict (without the oracle side) and the host copies of the timed outputs."""
+    import math
+    copies = max(1, math.ceil(ROTATE_BYTES / wl.alg_bytes) + 1)
+    if steps is None:  # a workload beside the headline: every copy read once
+        steps = copies
+    copies = min(copies, steps)
+    wl.replicate(copies)
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    g = capture(torch, wl.step, steps)
+    g.replay()  # untimed: first touch of code, page tables and every copy
+    torch.cuda.synchronize()
+    wl.poison_outputs()
+    ms = replay_ms(torch, g, steps, flush, mark=wl.w, idx=idx)
+    outs = wl.timed_outputs()
+    distinct = min(copies, steps) * wl.alg_bytes
+    log(f"[bench] w{wl.w}: {ms * 1e3:.2f} us per call over {steps} steps "
+        f"({copies} input copies, {distinct / 2**20:.0f} MiB of distinct reads)")
+    res = {"us_per_call": ms * 1e3, "ms_per_step": ms, "steps": steps,
+           "value": wl.units / (ms * 1e-3), "unit": wl.unit,
+           "timing": "hbm_cold", "input_copies": copies,
+           "distinct_read_bytes": distinct, "config": wl.describe()}
+    if extras:
+        res["steady_us_per_call"] = stats_us([replay_ms(torch, g, steps) for _ in range(3)])
+        del g
+        res["isolated_call_us"] = stats_us(isolated_ms(torch, wl.step, flush, 16))
+        res["isolated_empty_us"] = stats_us(isolated_ms(
+            torch, lambda i: idx.idx_floor_empty(1), flush, 8))
+        res["host_e2e_us_per_call"] = stats_us(host_e2e_ms(torch, wl.step, 16))
+        if wl.sorted_variant:
+            gs = capture(torch, lambda i: wl.step(i, sorted=True), steps)
+            gs.replay()
+            res["sorted_us_per_call"] = replay_ms(torch, gs, steps, flush) * 1e3
+            del gs
+        res["floor"] = floors(torch, idx, wl, steps, flush)
+        log(f"[bench] w{wl.w} floors: read {res['floor']['read_us']:.2f} us, read + hand-off "
+            f"{res['floor']['read_handoff_us']:.2f} us, empty {res['floor']['empty_us']:.2f} us")
+    else:
+        del g
+    res["roofline"] = roofline(wl, ms, read_traffic(wl.w))
+    return res, outs
+
+
+def cpu_baseline_leg(wl, outs, gpu_scores, seconds):
+    """The CPU oracle beside the GPU: checks the timed outputs against it (the
+    run fails on a mismatch), then times it on a bounded sample."""
+    parity = {"ok": True}
+    try:
+        parity.update(wl.parity(outs, gpu_scores))
+    except AssertionError as e:
+        parity = {"ok": False, "error": str(e)[:400]}
+    med, n = wl.oracle_time(seconds)
+    units = wl.oracle_units() if hasattr(wl, "oracle_units") else wl.units
+    base = {"value": units / med, "unit": wl.unit, "cores": blas_threads(), "kind": "oracle",
+            "sample": wl.sample_text(med, n) + "; numpy fp64 (BLAS threads for the products, "
+                      "the selection on one thread)", "cpu_model": cpu_model()}
+    return parity, base
+
+
 # ----------------------------------------------------------------------------------------
-# rocprofv3 --pmc output -> traffic summary
+# rocprofv3 output -> summaries
 # ----------------------------------------------------------------------------------------
 def parse_pmc(dirs, out_path, workload):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the benchmarked kernel, scaled
@@ -559,11 +805,63 @@ def parse_pmc(dirs, out_path, workload):
         for ctr, d in zip(("FETCH_SIZE", "WRITE_SIZE"), dirs):
             f.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d /root/repo/{d} -o pmc -- "
                     f"python3 /root/repo/bench.py --workload {workload} --steps 20 --warmup 5 "
-                    "--no-cpu-baseline --no-graph --no-extras --pmc-calibrate\n")
+                    "--no-cpu-baseline --no-extras --pmc-calibrate\n")
         f.write(f"#   python3 bench.py --workload {workload} --parse-pmc {' '.join(dirs)}\n")
         for k_, v in res.items():
             f.write(f"{k_}={v}\n")
     print(json.dumps(res))
+
+
+def parse_trace(d, out_path, command):
+    """Kernel statistics of each workload's timed region in a rocprofv3 kernel
+    trace of this script: the dispatches between the region's two marker
+    launches, grouped by kernel name."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def grid_wgs(r):
+        gx = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+        wx = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 1)) or 1)
+        return gx // max(wx, 1)
+
+    regions = {}
+    open_w = None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "floor_empty_kernel" in name:
+            n = grid_wgs(r)
+            if MARK_BEGIN < n < MARK_BEGIN + 100:
+                open_w = n - MARK_BEGIN
+                regions[open_w] = []
+                continue
+            if MARK_END < n < MARK_END + 100:
+                open_w = None
+                continue
+        if open_w is not None:
+            regions[open_w].append(r)
+    lines = [f"# Kernels of each workload's timed region (rocprofv3 kernel trace)", "",
+             "Command (run from /tmp on one MI355X, repository at /root/repo):", "", "```",
+             command, f"python3 bench.py --parse-trace {d}", "```", "",
+             "| workload | kernel | dispatches | average (us) | min (us) | max (us) |",
+             "|---|---|---|---|---|---|"]
+    for w in sorted(regions):
+        per = {}
+        for r in regions[w]:
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(r["Kernel_Name"].split("(")[0], []).append(dur)
+        for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {w} | `{k}` | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} "
+                         f"| {max(v):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def read_traffic(workload):
@@ -587,17 +885,19 @@ def read_traffic(workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time host-launched steps instead of a replayed HIP graph")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="CPU oracle timing budget per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (oracle timing and the parity check)")
     ap.add_argument("--pmc-calibrate", action="store_true")
     ap.add_argument("--parse-pmc", nargs="+", default=None)
+    ap.add_argument("--parse-trace", default=None)
+    ap.add_argument("--trace-command", default="")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the floor, cold, host end-to-end and sorted measurements")
+                    help="skip the steady, isolated, host end-to-end, sorted and floor figures")
     ap.add_argument("--out", default=None)
     a = ap.parse_args()
 
@@ -605,6 +905,10 @@ def main():
         out = a.out or os.path.join(ROOT, "profiles",
                                     f"traffic_w{a.workload}_{KERNEL[a.workload]}.txt")
         parse_pmc(a.parse_pmc, out, a.workload)
+        return 0
+    if a.parse_trace:
+        parse_trace(a.parse_trace, a.out or os.path.join(a.parse_trace, "regions.md"),
+                    a.trace_command)
         return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the indexer's "
@@ -619,128 +923,61 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
-
-    import synth
-    x0 = synth.workload(a.workload)
-    copies = max(1, min(256, -(-ROTATE_BYTES // input_bytes(a.workload, x0))))
-    del x0
-    log(f"[bench] workload {a.workload}: building inputs ({copies} copies)")
-    wl = make(a.workload, torch, idx, copies)
-
+    flush = Flusher(torch, idx)
     if a.pmc_calibrate:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    # eager: one host call per step (Python binding -> C ABI -> launch)
-    for i in range(a.warmup):
-        wl.step(i)
-    torch.cuda.synchronize()
-    n_eager = min(a.steps, 500)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(n_eager):
-        wl.step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / n_eager
+    head = a.workload if a.workload is not None else HEADLINE
+    order = [head] if a.workload is not None else [w for w in DEFAULT_SET if w != head] + [head]
+    results, failed = {}, []
+    for w in order:
+        log(f"[bench] workload {w}: building inputs")
+        wl = make(w, torch, idx)
+        res, outs = measure(torch, idx, wl, a.steps if w == head else None, a.warmup,
+                            not a.no_extras, flush)
+        if not a.no_cpu_baseline:
+            log(f"[bench] w{w}: CPU leg (oracle parity check, ~{a.cpu_seconds:.0f} s timing)")
+            res["parity"], res["cpu_baseline"] = cpu_baseline_leg(wl, outs, wl.gpu_scores(),
+                                                                  a.cpu_seconds)
+            if not res["parity"]["ok"]:
+                failed.append(w)
+                log(f"[bench] w{w}: PARITY FAILED: {res['parity']['error']}")
+        else:
+            res["parity"] = {"ok": None, "note": "not checked (--no-cpu-baseline)"}
+        res["dtype"] = wl.dtype
+        results[w] = res
+        del wl, outs
+        torch.cuda.empty_cache()
 
-    # timed region: the K steps captured once into a HIP graph and replayed, so
-    # the GPU runs the steps back to back without waiting on the host
-    graph = None
-    if not a.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(3):
-                wl.step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(a.steps):
-                wl.step(a.warmup + i)
-        graph.replay()  # untimed warm replay
-        torch.cuda.synchronize()
-    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps "
-        f"({'graph replay' if graph else 'eager'})")
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(a.steps):
-            wl.step(a.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / a.steps
-    log(f"[bench] {ms * 1e3:.2f} us per step (events), {wall / a.steps * 1e6:.2f} us wall, "
-        f"eager {eager_ms * 1e3:.2f} us per step")
-
-    launch_desc = "eager" if graph is None else f"hipGraph of {a.steps} steps"
-    extras = {}
-    if not a.no_extras:
-        # the same graph replayed again: spread of the steady-state figure
-        if graph is not None:
-            reps = []
-            for _ in range(4):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                graph.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                reps.append(e0.elapsed_time(e1) / a.steps)
-            extras["steady_us_per_call"] = stats_us([ms] + reps)
-        graph = None
-        log("[bench] cold calls, host end-to-end, floors")
-        extras["cold_us_per_call"] = stats_us(cold_times(torch, wl, 32))
-        extras["host_e2e_us_per_call"] = stats_us(host_e2e_times(torch, wl, 32))
-        if a.workload in (2, 3, 4, 6, 7):  # headline unsorted; the score-ordered output beside it
-            extras["sorted_us_per_call"] = min(graph_time(
-                torch, lambda i: wl.step(i, sorted=True), min(a.steps, 1000), 3)) * 1e3
-        extras["floor"] = floors(torch, idx, wl, min(a.steps, 200))
-        log(f"[bench] floors: {json.dumps(extras['floor'])}")
-
-    per_s = 1e3 / ms
-    if a.workload == 5:
-        bound, unit = "mfma", "TFLOP/s"
-        achieved = wl.alg_flops / (ms * 1e-3) / 1e12
-        peak = MFMA_BF16_PEAK_TFLOPS
-    else:
-        bound, unit = "hbm", "GB/s"
-        achieved = wl.alg_bytes / (ms * 1e-3) / 1e9
-        peak = HBM_PEAK_GBS
-    traffic = read_traffic(a.workload)
+    h = results[head]
     out = {
         "metric": METRIC,
-        "value": wl.units * per_s,
-        "unit": {5: "points/s", 3: "entries/s", 6: "page slots/s",
-                 7: "token-block pairs/s", 8: "blocks pooled/s"}.get(a.workload, "blocks/s"),
+        "value": h["value"], "unit": h["unit"],
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": ms, "us_per_call": ms * 1e3, "eager_us_per_call": eager_ms * 1e3,
-        "launch": launch_desc,
+        "ms_per_step": h["ms_per_step"], "us_per_call": h["us_per_call"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": wl.describe(),
-        "roofline": {"bound": bound, "kernel": KERNEL[a.workload], "achieved": achieved,
-                     "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": traffic,
-                     "alg_bytes_per_launch": wl.alg_bytes, "alg_flops_per_launch": wl.alg_flops},
+        "dtype": h["dtype"], "data": "synthetic",
+        "config": h["config"],
+        "timing": "hbm_cold: a HIP graph of the timed steps, replayed after a 1 GiB read "
+                  "that evicts L2 and the last-level cache; every step reads input copies "
+                  "no earlier step of the region touched",
+        "roofline": h["roofline"],
     }
-    if a.workload == 5:
-        out["roofline"]["hbm_frac"] = wl.alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
-    out.update(extras)
-    if not a.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle (~{a.cpu_seconds:.0f} s)")
-        v, sample = wl.cpu_oracle(a.cpu_seconds)
-        out["cpu_baseline"] = {"value": v, "unit": out["unit"], "cores": blas_threads(),
-                               "kind": "oracle", "sample": sample}
+    for k in ("parity", "cpu_baseline", "steady_us_per_call", "isolated_call_us",
+              "isolated_empty_us", "host_e2e_us_per_call", "sorted_us_per_call", "floor",
+              "input_copies", "distinct_read_bytes"):
+        if k in h:
+            out[k] = h[k]
+    if len(results) > 1:
+        out["workloads"] = {results[w]["config"]["workload"]: results[w]
+                            for w in order if w != head}
+    out["parity_all_ok"] = not failed if not a.no_cpu_baseline else None
     print(json.dumps(out), flush=True)
-    return 0
+    return 3 if failed else 0
 
 
 if __name__ == "__main__":

@@ -139,6 +139,12 @@ def _workspace(device, nbytes, kind):
     key = (kind, device.index, _stream(device))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            # a zero-filled allocation would be recorded into the graph (and its
+            # fill replayed with it): pass ws= to calls that are captured
+            raise RuntimeError(f"{kind}: no workspace for this stream while a graph is being "
+                               "captured; pass ws= (a zero-filled buffer of the size "
+                               "*_workspace_bytes returns)")
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
@@ -169,10 +175,10 @@ def idx_score(q, c, seq_len, page_size=16, scores=None):
     return scores
 
 
-def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None):
+def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None):
     """Row-wise top-K indices (ties to the lower index), padded with -1."""
     lib = load()
-    dev = _dev(scores, n_valid, ids, counts)
+    dev = _dev(scores, n_valid, ids, counts, ws)
     B, N = scores.shape
     if ids is None:
         ids = torch.empty(B, K, dtype=torch.int32, device=dev)
@@ -180,9 +186,11 @@ def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None):
         counts = torch.empty(B, dtype=torch.int32, device=dev)
     flags = IDX_SORTED if sorted else 0
     nbytes = lib.idx_topk_workspace_bytes(B, N, K, flags)
-    ws = _workspace(dev, nbytes, "topk") if nbytes else None
+    if ws is None and nbytes:
+        ws = _workspace(dev, nbytes, "topk")
     _check("idx_topk", lib.idx_topk(_ptr(scores), _ptr(n_valid), _ptr(ids), _ptr(counts), B, N, K,
-                                    flags, _ptr(ws), nbytes, _stream(dev)))
+                                    flags, _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(dev)))
     return ids, counts
 
 

@@ -63,3 +63,21 @@ def check_ids_band(ids_gpu, S, A, nv, K, rtol):
         kstar = int(ids_ref[b, :m][np.argmin(S[b, ids_ref[b, :m]])])
         for i in diff:
             assert abs(S[b, i] - S[b, kstar]) <= rtol * (A[b, i] + A[b, kstar]), (b, i, kstar)
+
+
+def check_assign(a, best, xb, cb, rows=None, rtol=RTOL["bf16"]):
+    """k-means assignment on the given rows: the GPU's winning value is half the
+    score of the centroid it chose (C2), and a winner other than the oracle's is
+    allowed only inside the tolerance band of the best score (C3). Returns the
+    number of rows whose winner differs."""
+    rows = np.arange(xb.shape[0]) if rows is None else rows
+    a_ref, S, A = oracle.assign(xb[rows], cb)
+    ag = a[rows]
+    i = np.arange(rows.size)
+    if best is not None:
+        np.testing.assert_array_less(np.abs(2.0 * best[rows] - S[i, ag]),
+                                     rtol * A[i, ag] + 1e-30)
+    off = np.nonzero(ag != a_ref)[0]
+    for k in off:
+        assert S[k, a_ref[k]] - S[k, ag[k]] <= rtol * (A[k, a_ref[k]] + A[k, ag[k]]), k
+    return off.size

@@ -13,7 +13,8 @@ torch = pytest.importorskip("torch")
 
 import oracle
 import synth
-from tests.helpers import RTOL, check_ids_band, check_ids_exact, check_scores, to_dev
+from tests.helpers import (RTOL, check_assign, check_ids_band, check_ids_exact, check_scores,
+                           to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -207,36 +208,6 @@ def test_select_workspace_reused_across_shapes():
         assert torch.equal(ids2, ids) and int(torch.count_nonzero(ws[:2 << 20])) == 0
 
 
-def test_select_graph_replays_match_eager():
-    """idx_select captured into a HIP graph: every replay equals the eager call."""
-    x = synth.make_indexer(4, 4, 128, 8192, [4096, 16384, 65536, 131072], 256, "bf16", 310)
-    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
-    ws = torch.zeros(idx.idx_workspace_bytes(4, 8192, 4, 256), dtype=torch.uint8, device="cuda")
-    ref, rc, _ = idx.idx_select(q, c, sl, 256, ws=ws)
-    ref, rc = ref.clone(), rc.clone()
-    ids = torch.full((4, 256), -7, dtype=torch.int32, device="cuda")
-    counts = torch.zeros(4, dtype=torch.int32, device="cuda")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        idx.idx_select(q, c, sl, 256, ids=ids, counts=counts, ws=ws)
-    torch.cuda.current_stream().wait_stream(side)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(3):
-            idx.idx_select(q, c, sl, 256, ids=ids, counts=counts, ws=ws)
-    for rep in range(4):
-        say(f"[select] graph replay {rep}")
-        ids.fill_(-7)
-        counts.zero_()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(ids, ref) and torch.equal(counts, rc), rep
-        eager, _, _ = idx.idx_select(q, c, sl, 256, ws=ws)  # eager work between replays
-        torch.cuda.synchronize()
-        assert torch.equal(eager, ref)
-
-
 def test_select_is_deterministic():
     x = synth.make_indexer(4, 4, 128, 8192, [4096, 16384, 65536, 131072], 256, "bf16", 305)
     a = run_select(x, 256, False, with_scores=True)
@@ -325,19 +296,6 @@ def run_assign(xb, cb):
     a, best = idx.idx_assign(to_dev(xb), to_dev(cb), return_best=True)
     torch.cuda.synchronize()
     return a.cpu().numpy(), best.cpu().numpy()
-
-
-def check_assign(a, best, xb, cb, rows=None):
-    rows = np.arange(xb.shape[0]) if rows is None else rows
-    a_ref, S, A = oracle.assign(xb[rows], cb)
-    ag = a[rows]
-    i = np.arange(rows.size)
-    # the GPU's winning value is half the score of the centroid it chose
-    np.testing.assert_array_less(np.abs(2.0 * best[rows] - S[i, ag]), RTOL["bf16"] * A[i, ag] + 1e-30)
-    off = np.nonzero(ag != a_ref)[0]
-    for k in off:  # a different winner only inside the tolerance band
-        assert S[k, a_ref[k]] - S[k, ag[k]] <= RTOL["bf16"] * (A[k, a_ref[k]] + A[k, ag[k]])
-    return off.size
 
 
 @pytest.mark.parametrize("N,C", [(1, 1), (1000, 100), (4097, 1024), (3000, 1031)])
