@@ -9,6 +9,7 @@ already resident in HBM. By default one run measures the five named workloads:
   3  top-K stress: 64 rows x 30000 fp32, nine distributions, K=2048  (idx_topk)
   4  large GQA decode batch: B=128, H=16, bf16, N_pad=2048, K=256     (idx_select)
   5  k-means assignment: 2^20 bf16 points x 1024 centroids, D=128     (idx_assign)
+  9  the top-K stress rows of workload 3 rounded to bf16               (idx_topk_bf16)
 
 The headline line is workload 4, the largest single-GPU indexer batch; the
 others are reported under "workloads", each with its own roofline.
@@ -37,7 +38,7 @@ algorithmic bytes, alone and followed by one cross-workgroup arrival counter,
 timed like the call).
 
 Other modes:
-  --workload N         one workload only (1..8; 6: paged pool, 7: prompt tokens,
+  --workload N         one workload only (1..9; 6: paged pool, 7: prompt tokens,
                        8: pooled keys), printed as the headline
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
   --parse-pmc DIR...   turn rocprofv3 --pmc output into a traffic summary
@@ -67,13 +68,13 @@ ROTATE_BYTES = 2 * LLC_BYTES    # distinct bytes read between two reads of one c
 FLUSH_BYTES = 1 << 30
 CALIB_BYTES = 1 << 30
 HEADLINE = 4
-DEFAULT_SET = (1, 2, 3, 4, 5)
+DEFAULT_SET = (1, 2, 3, 4, 5, 9)
 # empty launches with these workgroup counts bracket a workload's timed region
 MARK_BEGIN, MARK_END = 1000, 2000
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_split_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
-          7: "topk_kernel", 8: "pool_keys_kernel"}
+          7: "topk_kernel", 8: "pool_keys_kernel", 9: "topk_split_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
            ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "prefill.hip",
             "pool.hip", "api.cpp")]
@@ -231,7 +232,10 @@ class Topk(Workload):
     sorted_variant = True
 
     def __init__(self, x, torch, idx):
+        import numpy as np
         self.x, self.torch, self.idx = x, torch, idx
+        self.bf16 = x.scores.dtype == np.uint16   # bf16 rows go to idx_topk_bf16
+        self.dtype = "bf16" if self.bf16 else "f32"
         self.inputs = [(to_dev(x.scores),)]
         B, N = x.scores.shape
         self.ids = torch.empty(B, x.K, dtype=torch.int32, device="cuda")
@@ -239,7 +243,7 @@ class Topk(Workload):
         self.ws = torch.zeros(max(256, idx.idx_topk_workspace_bytes(B, N, x.K, 1)),
                               dtype=torch.uint8, device="cuda")
         self.units = B * N
-        self.alg_bytes = B * N * 4 + B * x.K * 4
+        self.alg_bytes = B * N * (2 if self.bf16 else 4) + B * x.K * 4
         self.alg_flops = 0
 
     def step(self, i, sorted=None):
@@ -254,12 +258,17 @@ class Topk(Workload):
 
     def describe(self):
         B, N = self.x.scores.shape
-        return {"workload": self.x.name, "call": "idx_topk", "rows": B, "N": N, "K": self.x.K,
-                "sorted": False, "inputs": "f32", "distributions": 9}
+        return {"workload": self.x.name, "call": "idx_topk_bf16" if self.bf16 else "idx_topk",
+                "rows": B, "N": N, "K": self.x.K, "sorted": False, "inputs": self.dtype,
+                "distributions": 9}
+
+    def values(self):
+        import oracle
+        return oracle.bf16_decode(self.x.scores) if self.bf16 else self.x.scores
 
     def oracle_call(self, i):
         import oracle
-        oracle.select(self.x.scores, None, self.x.K, False)
+        oracle.select(self.values(), None, self.x.K, False)
 
     def sample_text(self, med, n):
         return f"all {self.x.scores.shape[0]} rows, {n} calls, median {med * 1e3:.1f} ms per call"
@@ -268,7 +277,7 @@ class Topk(Workload):
         """C1 directly: the input scores are the GPU's own."""
         from tests.helpers import check_ids_exact
         ids, counts = outs
-        check_ids_exact(ids, counts, self.x.scores, None, self.x.K, False)
+        check_ids_exact(ids, counts, self.values(), None, self.x.K, False)
         return {"C1_ids_exact": True, "rows": int(self.x.scores.shape[0])}
 
 
@@ -552,7 +561,7 @@ def make(w, torch, idx):
     import synth
     x = synth.workload(w)
     cls = {1: Indexer, 2: Indexer, 3: Topk, 4: Indexer, 5: Assign, 6: Paged, 7: Prefill,
-           8: Pool}[w]
+           8: Pool, 9: Topk}[w]
     wl = cls(x, torch, idx)
     wl.w = w
     return wl
@@ -692,8 +701,8 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
     dict (without the oracle side) and the host copies of the timed outputs."""
     import math
     copies = max(1, math.ceil(ROTATE_BYTES / wl.alg_bytes) + 1)
-    if steps is None:  # a workload beside the headline: every copy read once
-        steps = copies
+    if steps is None:  # a workload beside the headline: every copy read, at least 12 steps
+        steps = max(copies, 12)
     copies = min(copies, steps)
     wl.replicate(copies)
     for i in range(warmup):
@@ -887,7 +896,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="CPU oracle timing budget per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true",

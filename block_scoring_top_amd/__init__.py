@@ -13,7 +13,7 @@ import threading
 
 import torch
 
-__all__ = ["idx_score", "idx_topk", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
+__all__ = ["idx_score", "idx_topk", "idx_topk_bf16", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
            "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
            "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
@@ -30,6 +30,8 @@ _SIGS = {
     "idx_score": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "idx_topk_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _u32]),
     "idx_topk": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _u32, _vp, _c_size, _vp]),
+    "idx_topk_bf16": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _u32, _vp, _c_size,
+                               _vp]),
     "idx_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _u32]),
     "idx_select": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _u32, _vp, _c_size, _vp]),
@@ -176,7 +178,10 @@ def idx_score(q, c, seq_len, page_size=16, scores=None):
 
 
 def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None):
-    """Row-wise top-K indices (ties to the lower index), padded with -1."""
+    """Row-wise top-K indices (ties to the lower index), padded with -1. float32
+    scores go to idx_topk, bfloat16 ones to idx_topk_bf16."""
+    if scores.dtype == torch.bfloat16:
+        return idx_topk_bf16(scores, K, n_valid, sorted, ids, counts, ws)
     lib = load()
     dev = _dev(scores, n_valid, ids, counts, ws)
     B, N = scores.shape
@@ -191,6 +196,27 @@ def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=No
     _check("idx_topk", lib.idx_topk(_ptr(scores), _ptr(n_valid), _ptr(ids), _ptr(counts), B, N, K,
                                     flags, _ptr(ws), 0 if ws is None else ws.numel(),
                                     _stream(dev)))
+    return ids, counts
+
+
+def idx_topk_bf16(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None):
+    """idx_topk over bfloat16 scores (16-bit keys, half the bytes read)."""
+    lib = load()
+    dev = _dev(scores, n_valid, ids, counts, ws)
+    if scores.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("idx_topk_bf16 takes bfloat16 scores")
+    B, N = scores.shape
+    if ids is None:
+        ids = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    flags = IDX_SORTED if sorted else 0
+    nbytes = lib.idx_topk_workspace_bytes(B, N, K, flags)
+    if ws is None and nbytes:
+        ws = _workspace(dev, nbytes, "topk")
+    _check("idx_topk_bf16", lib.idx_topk_bf16(_ptr(scores), _ptr(n_valid), _ptr(ids),
+                                              _ptr(counts), B, N, K, flags, _ptr(ws),
+                                              0 if ws is None else ws.numel(), _stream(dev)))
     return ids, counts
 
 

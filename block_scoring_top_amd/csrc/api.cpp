@@ -99,10 +99,18 @@ size_t idx_topk_workspace_bytes(int B, int N, int K, uint32_t flags) {
   return idxk::topk_split_workspace_bytes(B, N, K);
 }
 
-int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts, int B,
-             int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// idx_topk and idx_topk_bf16: the scores are fp32 (16-byte aligned) or bf16
+// (8-byte aligned).
+int topk_checked(const void* scores, bool bf16, const int32_t* n_valid, int32_t* ids,
+                 int32_t* counts, int B, int N, int K, uint32_t flags, void* ws, size_t ws_bytes,
+                 void* stream) {
   if (scores == nullptr || ids == nullptr) return IDX_ERR_INVALID_ARG;
-  if (!aligned(scores, 16) || !aligned(ids, 4) || !aligned(n_valid, 4) || !aligned(counts, 4))
+  if (!aligned(scores, bf16 ? 8 : 16) || !aligned(ids, 4) || !aligned(n_valid, 4) ||
+      !aligned(counts, 4))
     return IDX_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || K < 1) return IDX_ERR_INVALID_ARG;
   if (flags & ~IDX_SORTED) return IDX_ERR_INVALID_ARG;
@@ -113,7 +121,21 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
     return IDX_ERR_WORKSPACE;
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted,
-                                      need > 0 ? ws : nullptr, stream));
+                                      need > 0 ? ws : nullptr, stream, false, bf16));
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts, int B,
+             int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  return topk_checked(scores, false, n_valid, ids, counts, B, N, K, flags, ws, ws_bytes, stream);
+}
+
+int idx_topk_bf16(const uint16_t* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                  int B, int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  return topk_checked(scores, true, n_valid, ids, counts, B, N, K, flags, ws, ws_bytes, stream);
 }
 
 size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {

@@ -99,6 +99,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The workgroup barrier of the tile pipeline. The builtin alone is not a memory
+// operation to the compiler, which could then move LDS reads or the direct-to-
+// LDS refills across it; the empty asm statements with a memory clobber keep
+// them on their side without the vmcnt(0) that a workgroup fence would add.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 struct ArgmaxState {
   float best[kCB];
   int bidx[kCB];
@@ -187,7 +197,7 @@ __device__ __forceinline__ void assign_tile(const uint16_t* __restrict__ c,
   // (A plain barrier: the fence of __syncthreads would wait for every load.)
   if (refill) wait_vmcnt<kLoadsPerTile>();
   else wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
+  tile_barrier();
 }
 
 __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __restrict__ x,
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
   } else {
     wait_vmcnt<0>();
   }
-  __builtin_amdgcn_s_barrier();
+  tile_barrier();
 
   // unrolled by three so that every LDS access names its buffer at compile time
   for (int tile = 0; tile < ntiles; tile += 3) {

@@ -48,8 +48,15 @@ __global__ __launch_bounds__(kScoreNT) void score_kernel(const void* __restrict_
 // streamed through the register tile. ADAPTIVE (rows of any distribution):
 // the linear pass chooses its bins per row; otherwise value bins (dot-product
 // scores).
-template <bool SORTED, int NT, int SLOTS, bool ADAPTIVE = true>
-__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
+// BF16IN: the scores are bf16 (raw 16-bit patterns), selected with 16-bit keys.
+template <bool BF16IN>
+__device__ __forceinline__ const void* score_row(const void* scores, size_t off) {
+  return BF16IN ? static_cast<const void*>(static_cast<const uint16_t*>(scores) + off)
+                : static_cast<const void*>(static_cast<const float*>(scores) + off);
+}
+
+template <bool SORTED, int NT, int SLOTS, bool ADAPTIVE = true, bool BF16IN = false>
+__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ scores,
                                                   const int32_t* __restrict__ n_valid,
                                                   int32_t* __restrict__ ids,
                                                   int32_t* __restrict__ counts, int N, int K) {
@@ -58,9 +65,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   const int b = blockIdx.x;
   int n = N;
   if (n_valid != nullptr) n = max(0, min(n_valid[b], N));
-  select_row<NT, SLOTS, SORTED, false, false, IdsOut, ADAPTIVE>(
-      scores + (size_t)b * N, n, N, K, IdsOut{ids + (size_t)b * K}, counts ? counts + b : nullptr,
-      sm, sort_lds);
+  select_row<NT, SLOTS, SORTED, false, false, IdsOut, ADAPTIVE, BF16IN>(
+      score_row<BF16IN>(scores, (size_t)b * N), n, N, K, IdsOut{ids + (size_t)b * K},
+      counts ? counts + b : nullptr, sm, sort_lds);
 }
 
 // Long rows, few of them: each row is cut into S segments of L entries (L a
@@ -76,9 +83,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 // candidates fit one 2-slot tile, else 8, chosen on the host for score-ordered
 // merges (one merge per kernel keeps the registers of the 8-slot sort
 // unspilled); 0: chosen per call inside one kernel (index-order merges).
-template <bool SORTED, int MS>
+template <bool SORTED, int MS, bool BF16IN = false>
 __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ n_valid,
+    const void* __restrict__ scores, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, int N, int K, int S, int L,
     uint32_t* tickets, float* cand_score, int32_t* cand_id, int cstride) {
   // segments and index-order merges of at most 8192 keys use 2 key slots (one
@@ -106,20 +113,22 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     // where the emit's own stores would cover only its taken lanes.
     float* st_s = reinterpret_cast<float*>(smu.s2.hist[0]);
     int32_t* st_i = reinterpret_cast<int32_t*>(smu.s2.hist[1]);
-    select_row<kTopkNT, 2, false, false, false, StagedCandOut, true>(
-        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, StagedCandOut{st_s, st_i, lo},
-        nullptr, smu.s2, sort_lds);
+    select_row<kTopkNT, 2, false, false, false, StagedCandOut, true, BF16IN>(
+        score_row<BF16IN>(scores, (size_t)b * N + lo), seg_n, max(N - lo, 0), K,
+        StagedCandOut{st_s, st_i, lo}, nullptr, smu.s2, sort_lds);
     __syncthreads();
     for (int k = threadIdx.x; k < K; k += kTopkNT) {
       __hip_atomic_store(cand.score + k, st_s[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(cand.id + k, st_i[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (L <= kTopkNT * 2 * 4) {
-    select_row<kTopkNT, 2, false, false, false, CandOut, true>(
-        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, smu.s2, sort_lds);
+    select_row<kTopkNT, 2, false, false, false, CandOut, true, BF16IN>(
+        score_row<BF16IN>(scores, (size_t)b * N + lo), seg_n, max(N - lo, 0), K, cand, nullptr,
+        smu.s2, sort_lds);
   } else {
-    select_row<kTopkNT, kTopkSlots, false, false, false>(
-        scores + (size_t)b * N + lo, seg_n, max(N - lo, 0), K, cand, nullptr, sm, sort_lds);
+    select_row<kTopkNT, kTopkSlots, false, false, false, CandOut, true, BF16IN>(
+        score_row<BF16IN>(scores, (size_t)b * N + lo), seg_n, max(N - lo, 0), K, cand, nullptr,
+        sm, sort_lds);
   }
   // hand-off: as in the fused select (agent-scope stores, all memory operations
   // of the workgroup complete, one relaxed agent-scope ticket)
@@ -136,11 +145,12 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     __hip_atomic_store(&tickets[(size_t)b * kTicketStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   const MappedIdsOut out{ids + (size_t)b * K, ri};
+  // the candidates of bf16 rows are bf16 values (in fp32): 16-bit keys
   if (MS == 2 || (MS == 0 && S * K <= kTopkNT * 2 * 4))
-    select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true>(
+    select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true, false, BF16IN>(
         rs, S * K, cstride, K, out, counts ? counts + b : nullptr, smu.s2, sort_lds);
   else
-    select_row<kTopkNT, kTopkSlots, SORTED, true, false, MappedIdsOut, true>(
+    select_row<kTopkNT, kTopkSlots, SORTED, true, false, MappedIdsOut, true, false, BF16IN>(
         rs, S * K, cstride, K, out, counts ? counts + b : nullptr, sm, sort_lds);
 }
 
@@ -255,8 +265,57 @@ int topk_segments(int B, int N, int K) {
   return S;
 }
 
-int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
-                int B, int N, int K, bool sorted, void* split_ws, void* stream, bool dot_scores) {
+// bf16 rows (any distribution, adaptive bins): the same shapes as the fp32
+// rows, without the dot-product instances.
+int launch_topk_bf16(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                     int B, int N, int K, bool sorted, void* split_ws, void* stream) {
+  const dim3 grid((unsigned)B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int S = split_ws != nullptr ? topk_segments(B, N, K) : 1;
+  if (S > 1) {
+    const int L = ((N + S - 1) / S + 3) / 4 * 4;
+    const int cstride = (S * K + 3) / 4 * 4;
+    char* w = static_cast<char*>(split_ws);
+    uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
+    float* cs = reinterpret_cast<float*>(w + topk_ticket_bytes(B));
+    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_ticket_bytes(B) + (size_t)B * cstride * 4);
+    const dim3 g2((unsigned)((int64_t)B * S));
+    const bool merge2 = (int64_t)S * K <= kTopkNT * 2 * 4;
+#define IDX_LAUNCH_SPLIT16(SO, MS)                                                             \
+  hipLaunchKernelGGL((topk_split_kernel<SO, MS, true>), g2, dim3(kTopkNT),                     \
+                     SO ? sort_lds_bytes(K) : 0, s, scores, n_valid, ids, counts, N, K, S, L,  \
+                     tickets, cs, ci, cstride)
+    if (sorted) {
+      if (merge2) IDX_LAUNCH_SPLIT16(true, 2);
+      else IDX_LAUNCH_SPLIT16(true, kTopkSlots);
+    } else {
+      IDX_LAUNCH_SPLIT16(false, 0);
+    }
+#undef IDX_LAUNCH_SPLIT16
+    return (int)hipGetLastError();
+  }
+  const bool narrow = B >= 512 && N <= 2048 && (!sorted || K <= 1024);
+#define IDX_LAUNCH_TOPK16(SO, NT_, SL_)                                                       \
+  hipLaunchKernelGGL((topk_kernel<SO, NT_, SL_, true, true>), grid, dim3(NT_),               \
+                     SO ? sort_lds_bytes(K) : 0, s, scores, n_valid, ids, counts, N, K)
+  if (narrow) {
+    if (sorted) IDX_LAUNCH_TOPK16(true, 256, 2);
+    else IDX_LAUNCH_TOPK16(false, 256, 2);
+  } else if (N <= kTopkNT * 2 * 4) {
+    if (sorted) IDX_LAUNCH_TOPK16(true, kTopkNT, 2);
+    else IDX_LAUNCH_TOPK16(false, kTopkNT, 2);
+  } else {
+    if (sorted) IDX_LAUNCH_TOPK16(true, kTopkNT, kTopkSlots);
+    else IDX_LAUNCH_TOPK16(false, kTopkNT, kTopkSlots);
+  }
+#undef IDX_LAUNCH_TOPK16
+  return (int)hipGetLastError();
+}
+
+int launch_topk(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                int B, int N, int K, bool sorted, void* split_ws, void* stream, bool dot_scores,
+                bool bf16) {
+  if (bf16) return launch_topk_bf16(scores, n_valid, ids, counts, B, N, K, sorted, split_ws, stream);
   const dim3 grid((unsigned)B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int S = split_ws != nullptr ? topk_segments(B, N, K) : 1;

@@ -17,9 +17,12 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
 // dot_scores: rows of dot-product scores (value bins in the linear pass of
 // rows up to 8192 entries); otherwise rows of any distribution (bins chosen
 // per row).
-int launch_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+// bf16: the scores are bf16 (raw 16-bit patterns, any distribution).
+int launch_topk(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
                 int B, int N, int K, bool sorted, void* split_ws, void* stream,
-                bool dot_scores = false);
+                bool dot_scores = false, bool bf16 = false);
+int launch_topk_bf16(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                     int B, int N, int K, bool sorted, void* split_ws, void* stream);
 size_t topk_split_workspace_bytes(int B, int N, int K);
 
 // indptr == nullptr: dense tables (c is [B, N_pad, 128], seq_len gives the

@@ -48,11 +48,26 @@ namespace idxk {
 
 constexpr int kMaxSortedK = 4096;
 
-constexpr int kPasses = 3;
+// Radix digits of the order keys. 32-bit keys: 11 + 11 + 10 bits. Keys of
+// bf16 scores (KEY16) carry only 16 bits of information: the low half of the
+// fp32 pattern is zero, so the low half of the key is 0x0000 for non-negative
+// scores and 0xFFFF for negative ones; two digits of 11 + 5 bits resolve them
+// ("Iterate Topk", section 6: a 16-bit radix for the bottom-zero bf16 keys).
+constexpr int kPasses = 3;  // the most passes of any key width (and "key resolved")
+template <bool KEY16>
+__device__ __forceinline__ int n_passes() { return KEY16 ? 2 : 3; }
+template <bool KEY16>
 __device__ __forceinline__ int digit_shift(int p) {
-  return p == 0 ? kDigit0Shift : (p == 1 ? 10 : 0);
+  return p == 0 ? kDigit0Shift : (KEY16 ? 16 : (p == 1 ? 10 : 0));
 }
-__device__ __forceinline__ uint32_t digit_mask(int p) { return p == 2 ? 0x3FFu : 0x7FFu; }
+template <bool KEY16>
+__device__ __forceinline__ int digit_bits(int p) {
+  return p == 0 ? 11 : (KEY16 ? 5 : (p == 1 ? 11 : 10));
+}
+// the whole key of a bf16 score from its 16 significant bits
+__device__ __forceinline__ uint32_t key16_full(uint32_t top) {
+  return (top << 16) | ((top & 0x8000u) ? 0u : 0xFFFFu);
+}
 
 template <int NT, int SLOTS>
 struct SelectSmem {
@@ -79,11 +94,45 @@ struct SelectSmem {
 // (never candidates); otherwise entries are read one by one.
 // With COHERENT every entry is read with an agent-scope load, which sees data
 // that other workgroups wrote with agent-scope stores, on any XCD.
-template <int NT, int SLOTS, bool COHERENT>
-__device__ __forceinline__ void load_keys(const float* row, int n, int cap, int base,
+// BF16IN: the row holds bf16 scores (raw 16-bit patterns); every group of 4 is
+// one 8-byte load when the row is 8-byte aligned, and each value is widened to
+// its exact fp32 bits before the key transform.
+template <int NT, int SLOTS, bool COHERENT, bool BF16IN = false>
+__device__ __forceinline__ void load_keys(const void* row_v, int n, int cap, int base,
                                           uint32_t (&keys)[SLOTS][4]) {
+  static_assert(!(COHERENT && BF16IN), "bf16 rows are caller inputs, not staged rows");
   const int t = threadIdx.x;
+  const float* row = static_cast<const float*>(row_v);
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(row);
+  if constexpr (BF16IN) {
+    const uint16_t* h = static_cast<const uint16_t*>(row_v);
+    const bool aligned4h = (((uintptr_t)h & 7) == 0) && (cap & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (base + i * NT * 4 < n) {  // uniform: some thread of the workgroup has data here
+        const int e0 = base + (i * NT + t) * 4;
+        if (aligned4h) {
+          const uint2 v = *reinterpret_cast<const uint2*>(h + (e0 < n ? e0 : 0));
+          keys[i][0] = v.x << 16;
+          keys[i][1] = v.x & 0xFFFF0000u;
+          keys[i][2] = v.y << 16;
+          keys[i][3] = v.y & 0xFFFF0000u;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) keys[i][j] = (uint32_t)h[e0 + j < n ? e0 + j : 0] << 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = base + (i * NT + t) * 4 + j;
+        keys[i][j] = e < n ? order_key(__uint_as_float(keys[i][j])) : kKeyNegInf;
+      }
+    }
+    return;
+  }
   const bool aligned4 = (((uintptr_t)row & 15) == 0) && (cap & 3) == 0;
   if (COHERENT && aligned4) {
     // 16-byte buffer loads with the device-scope cache policy (sc1); the buffer
@@ -615,9 +664,12 @@ __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uin
 // blocked layout. Otherwise any n, in the striped layout (streamed tile by tile
 // when it does not fit one register tile). ADAPTIVE: the linear pass of a
 // striped row chooses value or key bins from the mean of its scores.
+// BF16IN: the row holds bf16 scores (striped rows only). KEY16: every key is
+// that of a bf16 score (bf16 rows, or candidates taken from them), so two
+// radix digits resolve a key.
 template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut,
-          bool ADAPTIVE = (!BLOCKED && SLOTS >= 8)>
-__device__ __attribute__((always_inline)) void select_row(const float* row, int n, int cap, int K,
+          bool ADAPTIVE = (!BLOCKED && SLOTS >= 8), bool BF16IN = false, bool KEY16 = BF16IN>
+__device__ __attribute__((always_inline)) void select_row(const void* row, int n, int cap, int K,
                                                          const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
                                                          uint64_t* sortbuf) {
@@ -626,6 +678,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   constexpr int E = SLOTS * NW;
   static_assert(NT >= 256 && NT <= 1024 && NT % 256 == 0,
                 "256 to 1024 threads: the bin search gives each thread 2 to 8 bins");
+  static_assert(!(BF16IN && BLOCKED), "bf16 rows use the striped layout");
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
@@ -643,9 +696,10 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   uint32_t raw[BLOCKED ? SLOTS : 1][4];  // blocked rows: the scores' bits as loaded
   uint32_t pay[kPay ? SLOTS : 1][4];     // striped rows with a payload: out.map's entries
   if constexpr (BLOCKED) {
-    load_keys_blocked<NT, SLOTS, COHERENT>(row, n, cap, kpt4, keys, raw);
+    load_keys_blocked<NT, SLOTS, COHERENT>(static_cast<const float*>(row), n, cap, kpt4, keys,
+                                          raw);
   } else if (cached) {
-    load_keys<NT, SLOTS, COHERENT>(row, n, cap, 0, keys);
+    load_keys<NT, SLOTS, COHERENT, BF16IN>(row, n, cap, 0, keys);
     if constexpr (kPay) load_payload<NT, SLOTS>(out.map, n, cap, 0, pay);
   }
 
@@ -909,12 +963,12 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   // Each pass histograms the next digit of the keys that still match the
   // resolved prefix, then finds the bin holding the need-th largest of them
   // (wave 0, find_bin above).
-  for (int p = 0; p < (resolved ? 0 : kPasses); ++p) {
+  for (int p = 0; p < (resolved ? 0 : n_passes<KEY16>()); ++p) {
     const int buf = (p + boff) & 1;
     uint32_t* h = sm.hist[buf];
-    const int shift = digit_shift(p);
-    const uint32_t dmask = digit_mask(p);
-    const int hshift = p == 0 ? 0 : digit_shift(p - 1);  // the resolved bits sit above this
+    const int shift = digit_shift<KEY16>(p);
+    const uint32_t dmask = (1u << digit_bits<KEY16>(p)) - 1u;
+    const int hshift = p == 0 ? 0 : digit_shift<KEY16>(p - 1);  // the resolved bits sit above this
     // this pass takes the range of its keys
     const bool track = (p == 0 && !upfront) || (!BLOCKED && p == 1);
     if (p == 1) {
@@ -922,7 +976,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       kmax = 0u;
     }
     for (int tile = 0; tile < ntiles; ++tile) {
-      if (!cached) load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
+      if (!cached) load_keys<NT, SLOTS, COHERENT, BF16IN>(row, n, cap, tile * TILE, keys);
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
         if (!slot_live(tile * TILE, i)) continue;
@@ -975,12 +1029,16 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
       level = kPasses;
       break;
     }
-    prefix = (prefix << (p == 2 ? 10 : 11)) | sm.sel_bin;
+    prefix = (prefix << digit_bits<KEY16>(p)) | sm.sel_bin;
     need = sm.sel_need;
     level = p + 1;
+    if (KEY16 && p == 1) {  // the 16 significant bits fix the whole key
+      prefix = key16_full(prefix);
+      level = kPasses;
+    }
     if (sm.sel_tot == need) {  // the whole bin is taken: every key from its lowest on
       simple = true;
-      t_lo = prefix << digit_shift(p);
+      t_lo = level == kPasses ? prefix : prefix << digit_shift<KEY16>(p);
       break;
     }
   }
@@ -995,7 +1053,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
     simple = true;
     t_lo = kKeyNegInf + 1u;
   }
-  const int shiftL = level == 1 ? kDigit0Shift : (level == 2 ? 10 : 0);
+  const int shiftL = level == 1 ? kDigit0Shift : (level == 2 ? 10 : 0);  // (KEY16: 1 or kPasses)
   const uint32_t lo_b = simple ? t_lo : prefix << shiftL;
   const uint32_t hi_b = simple ? t_lo - 1u : lo_b | ((1u << shiftL) - 1u);
   const uint32_t need_e = simple ? 0u : need;
@@ -1113,7 +1171,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* row, int 
   for (int tile = 0; tile < ((BLOCKED || by_bins) ? 0 : ntiles); ++tile) {
     if (!cached) {
       __syncthreads();  // the previous tile's counts have been read
-      load_keys<NT, SLOTS, COHERENT>(row, n, cap, tile * TILE, keys);
+      load_keys<NT, SLOTS, COHERENT, BF16IN>(row, n, cap, tile * TILE, keys);
       if constexpr (kPay) load_payload<NT, SLOTS>(out.map, n, cap, tile * TILE, pay);
     }
 #pragma unroll

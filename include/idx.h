@@ -126,6 +126,19 @@ int idx_topk(const float* scores, const int32_t* n_valid, int32_t* ids, int32_t*
              int B, int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * idx_topk_bf16 -- idx_topk over bf16 scores ("Iterate Topk", section 6: a
+ * 16-bit radix for bf16 scores, whose fp32 patterns have a zero low half).
+ * The same selection rule, outputs, workspace (idx_topk_workspace_bytes) and
+ * errors as idx_topk; scores compare as the exact fp32 values of the bf16
+ * patterns (-0.0 == +0.0, -inf never selected). Half the bytes of fp32 scores
+ * are read, and a key is resolved by at most two radix digits (11 + 5 bits).
+ *   scores [B,N] bf16 as raw 16-bit patterns, 8-byte aligned (rows of N % 4 != 0
+ *          are read entry by entry)
+ */
+int idx_topk_bf16(const uint16_t* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                  int B, int N, int K, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * idx_select -- fused score + mask + top-K ([CS] scorer feeding the top-K
  * stage; [QS] section 1, "combined" = score then select). Same inputs as
  * idx_score and the same selection rule as idx_topk applied to the scores that

@@ -329,6 +329,7 @@ WORKLOADS = {
     6: "paged pool: B=64 H=4 D=128 bf16, pages per request N(4096,1024) of 16384, K=256",
     7: "prompt tokens: B=2 T=512 H=4 D=128 bf16, pos0 {4096, 30000}, N_pad=1920, K=256",
     8: "pooled keys: B=4 bf16 keys, seq_len {4096, 16384, 65536, 131072}, 16-token blocks",
+    9: "top-K stress in bf16: the 64 x 30000 stress rows rounded to bf16, K=2048",
 }
 
 
@@ -362,4 +363,9 @@ def workload(n: int, seed: int | None = None):
     if n == 8:
         return make_keys(4, 131072, 128, 8192, [4096, 16384, 65536, 131072], "bf16", s,
                          name="w8_pool_keys_bf16")
+    if n == 9:
+        # the rows of the top-K stress workload (its seed, 3, unless one is given)
+        x = make_topk(64, 30000, 2048, 3 if seed is None else seed, name="w9_topk_stress_bf16")
+        x.scores = f32_to_bf16_bits(x.scores)
+        return x
     raise ValueError(n)

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["idx_score", "idx_topk", "idx_select", "idx_select_noalloc", "idx_select_paged",
+    for n in ["idx_score", "idx_topk", "idx_topk_bf16", "idx_select", "idx_select_noalloc",
+              "idx_select_paged",
               "idx_select_prefill",
               "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign",
               "idx_workspace_bytes",
@@ -117,6 +118,24 @@ def topk_call(lib, **kw):
 ])
 def test_topk_rejects(lib, kw, want):
     assert topk_call(lib, **kw) == want
+
+
+def topk_bf16_call(lib, **kw):
+    a = dict(scores=P, n_valid=None, ids=P, counts=None, B=2, N=100, K=10, flags=0, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return lib.idx_topk_bf16(a["scores"], a["n_valid"], a["ids"], a["counts"], a["B"], a["N"],
+                             a["K"], a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(scores=None), INVALID), (dict(ids=None), INVALID), (dict(scores=P + 4), INVALID),
+    (dict(scores=P + 2), INVALID), (dict(ids=P + 2), INVALID), (dict(n_valid=P + 1), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(K=0), INVALID), (dict(flags=0x80), INVALID),
+    (dict(K=4097, flags=1), UNSUPPORTED), (dict(B=64, N=30000, K=2048), WORKSPACE),
+])
+def test_topk_bf16_rejects(lib, kw, want):
+    assert topk_bf16_call(lib, **kw) == want
 
 
 def select_call(lib, **kw):
