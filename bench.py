@@ -10,6 +10,7 @@ already resident in HBM. By default one run measures the five named workloads:
   4  large GQA decode batch: B=128, H=16, bf16, N_pad=2048, K=256     (idx_select)
   5  k-means assignment: 2^20 bf16 points x 1024 centroids, D=128     (idx_assign)
   9  the top-K stress rows of workload 3 rounded to bf16               (idx_topk_bf16)
+ 10  clustered rows: 64 x 8000, tight cluster + wide outliers, K=1024 (idx_topk)
 
 The headline line is workload 4, the largest single-GPU indexer batch; the
 others are reported under "workloads", each with its own roofline.
@@ -19,7 +20,8 @@ How a workload is timed ("hbm_cold"):
     reads (its algorithmic bytes, not the padded allocation) add up to at least
     twice the 256 MiB last-level cache between two reads of the same copy;
   - the timed steps (step i reads copy i mod copies) are captured once into a
-    HIP graph; the graph is replayed once untimed;
+    HIP graph; the graph is replayed untimed for at least 20 ms (clocks ramp
+    up after the host's pauses);
   - then a 1 GiB streaming read evicts L2 and the last-level cache (a read, so
     that no dirty lines are left whose write-back would be charged to the call);
   - then the graph is replayed between HIP events on the replaying stream, with
@@ -38,7 +40,7 @@ algorithmic bytes, alone and followed by one cross-workgroup arrival counter,
 timed like the call).
 
 Other modes:
-  --workload N         one workload only (1..9; 6: paged pool, 7: prompt tokens,
+  --workload N         one workload only (1..10; 6: paged pool, 7: prompt tokens,
                        8: pooled keys), printed as the headline
   --pmc-calibrate      also run a plain 1 GiB device copy (for byte counters)
   --parse-pmc DIR...   turn rocprofv3 --pmc output into a traffic summary
@@ -68,13 +70,13 @@ ROTATE_BYTES = 2 * LLC_BYTES    # distinct bytes read between two reads of one c
 FLUSH_BYTES = 1 << 30
 CALIB_BYTES = 1 << 30
 HEADLINE = 4
-DEFAULT_SET = (1, 2, 3, 4, 5, 9)
+DEFAULT_SET = (1, 2, 3, 4, 5, 9, 10)
 # empty launches with these workgroup counts bracket a workload's timed region
 MARK_BEGIN, MARK_END = 1000, 2000
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_split_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
-          7: "topk_kernel", 8: "pool_keys_kernel", 9: "topk_split_kernel"}
+          7: "topk_kernel", 8: "pool_keys_kernel", 9: "topk_split_kernel", 10: "topk_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
            ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "prefill.hip",
             "pool.hip", "api.cpp")]
@@ -260,7 +262,7 @@ class Topk(Workload):
         B, N = self.x.scores.shape
         return {"workload": self.x.name, "call": "idx_topk_bf16" if self.bf16 else "idx_topk",
                 "rows": B, "N": N, "K": self.x.K, "sorted": False, "inputs": self.dtype,
-                "distributions": 9}
+                "distributions": sorted(set(self.x.dists))}
 
     def values(self):
         import oracle
@@ -561,7 +563,7 @@ def make(w, torch, idx):
     import synth
     x = synth.workload(w)
     cls = {1: Indexer, 2: Indexer, 3: Topk, 4: Indexer, 5: Assign, 6: Paged, 7: Prefill,
-           8: Pool, 9: Topk}[w]
+           8: Pool, 9: Topk, 10: Topk}[w]
     wl = cls(x, torch, idx)
     wl.w = w
     return wl
@@ -709,8 +711,14 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
         wl.step(i)
     torch.cuda.synchronize()
     g = capture(torch, wl.step, steps)
-    g.replay()  # untimed: first touch of code, page tables and every copy
-    torch.cuda.synchronize()
+    # untimed: first touch of code, page tables and every copy, then replays for
+    # at least 20 ms so that the GPU clocks have ramped up after the host's pause
+    t_end = time.perf_counter() + 0.02
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     wl.poison_outputs()
     ms = replay_ms(torch, g, steps, flush, mark=wl.w, idx=idx)
     outs = wl.timed_outputs()
@@ -896,7 +904,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
+    ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 11)))
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="CPU oracle timing budget per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true",

@@ -297,6 +297,16 @@ def topk_row(rng, dist: str, n: int) -> np.ndarray:
     raise ValueError(dist)
 
 
+def clustered_rows(rng, B, N, sigma=0.2, wide=10.0, frac=0.05):
+    """Rows whose scores form a tight cluster (N(0, sigma)) plus a fraction of
+    wide outliers (N(0, wide)) that stretch the row's range: the linear bin of
+    the K-th score then holds hundreds of distinct keys."""
+    v = rng.normal(0.0, sigma, (B, N))
+    out = rng.random((B, N)) < frac
+    v[out] = rng.normal(0.0, wide, int(out.sum()))
+    return v.astype(np.float32)
+
+
 def make_topk(B, N, K, seed, dists=None, name="custom"):
     rng = np.random.default_rng(seed)
     dists = TOPK_DISTS if dists is None else dists
@@ -330,6 +340,7 @@ WORKLOADS = {
     7: "prompt tokens: B=2 T=512 H=4 D=128 bf16, pos0 {4096, 30000}, N_pad=1920, K=256",
     8: "pooled keys: B=4 bf16 keys, seq_len {4096, 16384, 65536, 131072}, 16-token blocks",
     9: "top-K stress in bf16: the 64 x 30000 stress rows rounded to bf16, K=2048",
+    10: "clustered top-K rows: 64 x 8000 fp32, 95% N(0, 0.2) and 5% N(0, 10), K=1024",
 }
 
 
@@ -368,4 +379,8 @@ def workload(n: int, seed: int | None = None):
         x = make_topk(64, 30000, 2048, 3 if seed is None else seed, name="w9_topk_stress_bf16")
         x.scores = f32_to_bf16_bits(x.scores)
         return x
+    if n == 10:
+        rng = np.random.default_rng(s)
+        return TopkInputs(scores=clustered_rows(rng, 64, 8000), K=1024, dists=["clustered"] * 64,
+                          name="w10_topk_clustered")
     raise ValueError(n)

@@ -56,6 +56,19 @@ def test_workload_shapes_and_structure():
     assert w4.seq_len.min() >= 8192 and w4.seq_len.max() <= 32768
 
 
+def test_bf16_and_clustered_topk_workloads():
+    w3, w9 = synth.workload(3), synth.workload(9)
+    assert w9.scores.dtype == np.uint16 and w9.scores.shape == w3.scores.shape
+    # workload 9 is workload 3's rows rounded to bf16
+    np.testing.assert_array_equal(w9.scores, synth.f32_to_bf16_bits(w3.scores))
+    w10 = synth.workload(10)
+    assert w10.scores.shape == (64, 8000) and w10.K == 1024
+    v = w10.scores
+    inside = np.abs(v) < 1.0
+    assert 0.9 < inside.mean() < 0.99            # the tight cluster
+    assert np.abs(v).max() > 20.0                # the wide outliers stretch the range
+
+
 def test_assign_generator_structure():
     x = synth.make_assign(1000, 64, 128, 5)
     assert x.x.shape == (1000, 128) and x.c.shape == (64, 128)
