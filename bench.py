@@ -35,7 +35,9 @@ without a flush), isolated_call_us (one call after a flush, HIP events around
 that call alone; isolated_empty_us is an empty launch timed the same way, the
 events' own overhead), host_e2e_us_per_call (host wall clock of one call plus a
 synchronise), sorted_us_per_call (score-ordered output where the headline is
-id-ordered), and floor (an empty launch, and a streaming read of the call's
+id-ordered), plan_host_e2e_us and plan_graph_host_e2e_us (the same through a
+resolved plan, and through a one-call graph of it), and floor (an empty
+launch, and a streaming read of the call's
 algorithmic bytes, alone and followed by one cross-workgroup arrival counter,
 timed like the call).
 
@@ -183,6 +185,29 @@ class Indexer(Workload):
 
     def out_tensors(self):
         return [self.ids, self.counts]
+
+    def plan_e2e(self, n):
+        """Host end-to-end of one call through a plan (idx_plan_select), and of
+        one replay of a graph holding one plan call, each plus a synchronise."""
+        torch, x = self.torch, self.x
+        dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        plan = self.idx.plan_for(x.B, x.H, x.N_pad, x.K, dt, x.page_size, x.sorted)
+        q, c, sl = self.inputs[0]
+        g = plan.capture(q, c, sl, self.ids, self.counts)
+        out = {}
+        for key, fn in (("plan_host_e2e_us", lambda: plan(q, c, sl, self.ids, self.counts)),
+                        ("plan_graph_host_e2e_us", g.replay)):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(n):
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e3)
+            out[key] = stats_us(ts)
+        del g
+        return out
 
     def gpu_scores(self):
         """One more call that also writes the scores: the GPU's own fp32 scores
@@ -736,6 +761,8 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
         res["isolated_empty_us"] = stats_us(isolated_ms(
             torch, lambda i: idx.idx_floor_empty(1), flush, 8))
         res["host_e2e_us_per_call"] = stats_us(host_e2e_ms(torch, wl.step, 16))
+        if hasattr(wl, "plan_e2e"):
+            res.update(wl.plan_e2e(16))
         if wl.sorted_variant:
             gs = capture(torch, lambda i: wl.step(i, sorted=True), steps)
             gs.replay()
@@ -985,7 +1012,8 @@ def main():
         "roofline": h["roofline"],
     }
     for k in ("parity", "cpu_baseline", "steady_us_per_call", "isolated_call_us",
-              "isolated_empty_us", "host_e2e_us_per_call", "sorted_us_per_call", "floor",
+              "isolated_empty_us", "host_e2e_us_per_call", "plan_host_e2e_us",
+              "plan_graph_host_e2e_us", "sorted_us_per_call", "floor",
               "input_copies", "distinct_read_bytes"):
         if k in h:
             out[k] = h[k]

@@ -16,7 +16,8 @@ import torch
 __all__ = ["idx_score", "idx_topk", "idx_topk_bf16", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
            "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
-           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError"]
+           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError",
+           "SelectPlan", "plan_for"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libidx.so")
@@ -49,6 +50,11 @@ _SIGS = {
     "idx_assign": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int64, _c_int, _c_int, _c_int, _vp,
                             _c_size, _vp]),
     "idx_status_string": (ctypes.c_char_p, [_c_int]),
+    "idx_plan_create": (_c_int, [ctypes.POINTER(_vp), _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _u32]),
+    "idx_plan_workspace_bytes": (_c_size, [_vp]),
+    "idx_plan_select": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "idx_plan_destroy": (None, [_vp]),
     "idx_floor_empty": (_c_int, [_c_int, _vp]),
     "idx_floor_read": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _vp]),
 }
@@ -369,3 +375,84 @@ def idx_floor_read(src, nbytes, sink, ticket=None, blocks=256, threads=256):
         raise ValueError("idx_floor_read: buffer too small")
     _check("idx_floor_read", load().idx_floor_read(_ptr(src), nbytes, _ptr(sink), _ptr(ticket),
                                                    blocks, threads, _stream(dev)))
+
+
+class SelectPlan:
+    """idx_select for one call signature, resolved once by the library
+    (idx_plan_create: kernel instance, workgroup size and chunking fixed up
+    front), with its own zero-filled workspace on `device`. Calling it checks
+    only that the tensors match the signature; capture() records plan calls
+    into a HIP graph. Calls of one plan must not overlap (one workspace)."""
+
+    def __init__(self, B, H, N_pad, K, dtype=torch.bfloat16, page_size=16, sorted=False,
+                 device=None, chunk_log2=0):
+        lib = load()
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.B, self.H, self.N_pad, self.K, self.page_size = B, H, N_pad, K, page_size
+        self.dtype, self.sorted = dtype, sorted
+        flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+        handle = _vp()
+        _check("idx_plan_create", lib.idx_plan_create(
+            ctypes.byref(handle), B, H, 128, N_pad, page_size, K,
+            IDX_BF16 if dtype == torch.bfloat16 else IDX_F32, flags))
+        self._lib, self._handle = lib, handle
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.ws = torch.zeros(max(lib.idx_plan_workspace_bytes(handle), 256), dtype=torch.uint8,
+                              device=dev)
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value is not None:
+            self._lib.idx_plan_destroy(h)
+            self._handle = None
+
+    def __call__(self, q, c, seq_len, ids=None, counts=None, scores_out=None):
+        """Returns (ids, counts, scores_out or None), as idx_select does."""
+        dev = _dev(q, c, seq_len, ids, counts, scores_out)
+        if dev != self.device:
+            raise ValueError("the plan's workspace lives on another device")
+        if (tuple(q.shape) != (self.B, self.H, 128) or tuple(c.shape) != (self.B, self.N_pad, 128)
+                or q.dtype != self.dtype or c.dtype != self.dtype or seq_len.numel() != self.B):
+            raise ValueError("tensors do not match the plan's signature")
+        if ids is None:
+            ids = torch.empty(self.B, self.K, dtype=torch.int32, device=dev)
+        if counts is None:
+            counts = torch.empty(self.B, dtype=torch.int32, device=dev)
+        _check("idx_plan_select", self._lib.idx_plan_select(
+            self._handle, _ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts),
+            _ptr(scores_out), _ptr(self.ws), self.ws.numel(), _stream(dev)))
+        return ids, counts, scores_out
+
+    def capture(self, q, c, seq_len, ids, counts, scores_out=None, calls=1):
+        """A HIP graph of `calls` plan calls on these buffers (they must stay
+        alive while the graph is replayed); one eager call first runs on the
+        capturing stream."""
+        side = torch.cuda.Stream(self.device)
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            self(q, c, seq_len, ids, counts, scores_out)
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                self(q, c, seq_len, ids, counts, scores_out)
+        return g
+
+
+_plan_cache: dict = {}
+
+
+def plan_for(B, H, N_pad, K, dtype=torch.bfloat16, page_size=16, sorted=False, device=None):
+    """The cached SelectPlan of a signature (created on first use)."""
+    dev = torch.device(device if device is not None else "cuda")
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (B, H, N_pad, K, dtype, page_size, bool(sorted), index)
+    p = _plan_cache.get(key)
+    if p is None:
+        p = SelectPlan(B, H, N_pad, K, dtype, page_size, sorted, torch.device("cuda", index))
+        _plan_cache[key] = p
+    return p

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "idx.h"
 #include "launch.h"
 
@@ -78,6 +80,7 @@ const char* idx_status_string(int status) {
     case IDX_ERR_WORKSPACE: return "workspace missing or too small";
     case IDX_ERR_HIP: return "HIP launch failed";
     case IDX_ERR_SCRATCH: return "shape exceeds the static scratch of idx_select_noalloc";
+    case IDX_ERR_NO_MEMORY: return "host memory for the plan could not be allocated";
     default: return "unknown status";
   }
 }
@@ -148,37 +151,76 @@ size_t idx_workspace_bytes(int B, int N_pad, int H, int K, uint32_t flags) {
 
 namespace {
 
-// Argument checks shared by idx_select and idx_select_noalloc (everything but
-// the workspace).
-int check_select_args(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
-                      int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
-                      int page_size, int K, idx_dtype dt, uint32_t flags) {
-  int st = check_scoring_args(q, c, seq_len, B, H, D, N_pad, page_size, dt);
-  if (st != IDX_OK) return st;
-  if (ids == nullptr || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(scores_out, 4))
-    return IDX_ERR_INVALID_ARG;
+// The shape of an idx_select call (everything that a plan fixes).
+int check_select_shape(int B, int H, int D, int N_pad, int page_size, int K, idx_dtype dt,
+                       uint32_t flags) {
+  if (B < 1 || H < 1 || D < 1 || N_pad < 1 || page_size < 1) return IDX_ERR_INVALID_ARG;
+  if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
+  if ((int64_t)B * N_pad > kMaxRows) return IDX_ERR_INVALID_ARG;
   if (K < 1 || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
+  int st;
   if ((st = check_chunk_flag(flags)) != IDX_OK) return st;
+  if (H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
   if (B > kMaxRequests) return IDX_ERR_UNSUPPORTED;
   if ((flags & IDX_SORTED) != 0 && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
   return IDX_OK;
 }
 
-// Launch shape of the fused select, then the launch: 1024-thread workgroups for
-// a few requests, 512-thread ones for many; the score order of more than 1024
-// ids is sorted by 1024-thread workgroups only.
-int dispatch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
-                    int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
-                    int K, idx_dtype dt, uint32_t flags, uint32_t* tickets, float* stage,
-                    void* stream) {
+// The pointers of an idx_select call.
+int check_select_ptrs(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                      int32_t* counts, float* scores_out) {
+  if (q == nullptr || c == nullptr || seq_len == nullptr || ids == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(c, 16) || !aligned(seq_len, 4) || !aligned(ids, 4) ||
+      !aligned(counts, 4) || !aligned(scores_out, 4))
+    return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+// Argument checks shared by idx_select and idx_select_noalloc (everything but
+// the workspace).
+int check_select_args(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                      int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
+                      int page_size, int K, idx_dtype dt, uint32_t flags) {
+  const int st = check_select_shape(B, H, D, N_pad, page_size, K, dt, flags);
+  if (st != IDX_OK) return st;
+  return check_select_ptrs(q, c, seq_len, ids, counts, scores_out);
+}
+
+// The launch of a fused select, resolved from its shape: 1024-thread
+// workgroups for a few requests, 512-thread ones for many (the score order of
+// more than 1024 ids is sorted by 1024-thread workgroups only), and the rows
+// scored per workgroup.
+struct SelectLaunch {
+  int B, H, N_pad, page_size, K;
+  bool bf16, sorted, wide;
+  int chunk;
+};
+
+SelectLaunch resolve_select(int B, int H, int N_pad, int page_size, int K, idx_dtype dt,
+                            uint32_t flags) {
   const bool sorted = (flags & IDX_SORTED) != 0;
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
   const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
-  return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad,
-                                        page_size, K, dt == IDX_BF16, sorted, chunk, wide,
-                                        tickets, stage, stage_stride(N_pad), nullptr, nullptr, 0,
-                                        0, stream));
+  return SelectLaunch{B, H, N_pad, page_size, K, dt == IDX_BF16, sorted, wide, chunk};
+}
+
+int launch_resolved(const SelectLaunch& L, const void* q, const void* c, const int32_t* seq_len,
+                    int32_t* ids, int32_t* counts, float* scores_out, uint32_t* tickets,
+                    float* stage, void* stream) {
+  return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, L.B, L.H,
+                                        L.N_pad, L.page_size, L.K, L.bf16, L.sorted, L.chunk,
+                                        L.wide, tickets, stage, stage_stride(L.N_pad), nullptr,
+                                        nullptr, 0, 0, stream));
+}
+
+int dispatch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                    int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
+                    int K, idx_dtype dt, uint32_t flags, uint32_t* tickets, float* stage,
+                    void* stream) {
+  return launch_resolved(resolve_select(B, H, N_pad, page_size, K, dt, flags), q, c, seq_len,
+                         ids, counts, scores_out, tickets, stage, stream);
 }
 
 }  // namespace
@@ -217,6 +259,48 @@ int idx_select_noalloc(const void* q, const void* c, const int32_t* seq_len, int
   return dispatch_select(q, c, seq_len, ids, counts, scores_out, B, H, N_pad, page_size, K, dt,
                          flags, tickets, stage, stream);
 }
+
+}  // extern "C"
+
+// A resolved idx_select launch for one call signature (host memory only).
+struct idx_plan {
+  SelectLaunch launch;
+  size_t ws_bytes;
+};
+
+extern "C" {
+
+int idx_plan_create(idx_plan** plan, int B, int H, int D, int N_pad, int page_size, int K,
+                    idx_dtype dt, uint32_t flags) {
+  if (plan == nullptr) return IDX_ERR_INVALID_ARG;
+  *plan = nullptr;
+  const int st = check_select_shape(B, H, D, N_pad, page_size, K, dt, flags);
+  if (st != IDX_OK) return st;
+  idx_plan* p = new (std::nothrow) idx_plan{resolve_select(B, H, N_pad, page_size, K, dt, flags),
+                                            idx_workspace_bytes(B, N_pad, H, K, flags)};
+  if (p == nullptr) return IDX_ERR_NO_MEMORY;
+  *plan = p;
+  return IDX_OK;
+}
+
+size_t idx_plan_workspace_bytes(const idx_plan* plan) {
+  return plan == nullptr ? 0 : plan->ws_bytes;
+}
+
+int idx_plan_select(const idx_plan* plan, const void* q, const void* c, const int32_t* seq_len,
+                    int32_t* ids, int32_t* counts, float* scores_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (plan == nullptr) return IDX_ERR_INVALID_ARG;
+  const int st = check_select_ptrs(q, c, seq_len, ids, counts, scores_out);
+  if (st != IDX_OK) return st;
+  if (ws == nullptr || ws_bytes < plan->ws_bytes || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
+  uint32_t* tickets = static_cast<uint32_t*>(ws);
+  float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
+  return launch_resolved(plan->launch, q, c, seq_len, ids, counts, scores_out, tickets, stage,
+                         stream);
+}
+
+void idx_plan_destroy(idx_plan* plan) { delete plan; }
 
 int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr,
                      const int32_t* kv_indices, int32_t* ids, int32_t* counts, float* scores_out,

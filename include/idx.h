@@ -57,8 +57,9 @@ enum {
   IDX_ERR_UNSUPPORTED = -2, /* legal but not built: head_dim != 128, K > 4096 sorted */
   IDX_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
   IDX_ERR_HIP = -4,         /* the HIP runtime refused the launch              */
-  IDX_ERR_SCRATCH = -5      /* idx_select_noalloc: the shape needs more than its
+  IDX_ERR_SCRATCH = -5,     /* idx_select_noalloc: the shape needs more than its
                                static scratch holds                              */
+  IDX_ERR_NO_MEMORY = -6    /* idx_plan_create: no host memory for the plan      */
 };
 
 /* flags */
@@ -185,6 +186,32 @@ int idx_select(const void* q, const void* c, const int32_t* seq_len, int32_t* id
 int idx_select_noalloc(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
                        int32_t* counts, float* scores_out, int B, int H, int D, int N_pad,
                        int page_size, int K, idx_dtype dt, uint32_t flags, void* stream);
+
+/*
+ * Plans -- a resolved idx_select launch for one call signature ("Export Cake
+ * KMeans plan-runtime suite", Summary: a per-signature launch plan resolved
+ * once, then called many times; the plan's calls may be captured into a HIP
+ * graph, which the library leaves to the caller's stream capture).
+ *   idx_plan_create validates the shape (B, H, D, N_pad, page_size, K, dt,
+ *   flags: the rules and errors of idx_select) and resolves the launch (kernel
+ *   instance, workgroup size, blocks scored per workgroup) into a plan held in
+ *   host memory, owned by the caller until idx_plan_destroy; it makes no HIP
+ *   call. *plan is NULL on failure (IDX_ERR_NO_MEMORY: host allocation failed).
+ *   idx_plan_workspace_bytes: the workspace its calls need (that of idx_select).
+ *   idx_plan_select: idx_select with the plan's shape. Only the pointers, their
+ *   alignment and the workspace are checked; the ids, counts and scores are
+ *   those idx_select writes. A plan is read-only after creation and may be used
+ *   from several threads; calls that may overlap need distinct workspaces.
+ *   idx_plan_destroy(NULL) is a no-op.
+ */
+typedef struct idx_plan idx_plan;
+int idx_plan_create(idx_plan** plan, int B, int H, int D, int N_pad, int page_size, int K,
+                    idx_dtype dt, uint32_t flags);
+size_t idx_plan_workspace_bytes(const idx_plan* plan);
+int idx_plan_select(const idx_plan* plan, const void* q, const void* c, const int32_t* seq_len,
+                    int32_t* ids, int32_t* counts, float* scores_out, void* ws, size_t ws_bytes,
+                    void* stream);
+void idx_plan_destroy(idx_plan* plan);
 
 /*
  * idx_select_paged -- idx_select over a paged centroid pool ([CS] submission

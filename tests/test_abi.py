@@ -15,7 +15,7 @@ import block_scoring_top_amd as idx
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH, NOMEM = 0, -1, -2, -3, -4, -5, -6
 P = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
 
 
@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
               "idx_select_prefill",
               "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign",
               "idx_workspace_bytes",
-              "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string"]:
+              "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
+              "idx_plan_create", "idx_plan_select", "idx_plan_workspace_bytes", "idx_plan_destroy"]:
         assert n in names
 
 
@@ -54,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert idx.idx_status_string(OK) == "ok"
-    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH):
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH, NOMEM):
         assert idx.idx_status_string(s) not in ("ok", "unknown status")
     assert idx.idx_status_string(12345) == "unknown status"
 
@@ -304,3 +305,47 @@ def test_floor_launches_reject_bad_arguments(lib):
     assert r(P, 1024, P, None, 0, 256, None) == INVALID         # no workgroups
     assert r(P, 1024, P, None, 4, 512, None) == INVALID         # unsupported block size
     assert r(P, 1024, P, P + 2, 4, 256, None) == INVALID        # misaligned ticket
+
+
+def plan_create(lib, **kw):
+    a = dict(B=4, H=4, D=128, N_pad=8192, page_size=16, K=256, dt=1, flags=0)
+    a.update(kw)
+    h = ctypes.c_void_p(12345)
+    st = lib.idx_plan_create(ctypes.byref(h), a["B"], a["H"], a["D"], a["N_pad"], a["page_size"],
+                             a["K"], a["dt"], a["flags"])
+    return st, h
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(N_pad=0), INVALID),
+    (dict(page_size=0), INVALID), (dict(K=0), INVALID), (dict(dt=7), INVALID),
+    (dict(flags=0x4), INVALID), (dict(flags=3 << 8), INVALID), (dict(D=64), UNSUPPORTED),
+    (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
+    (dict(B=16385, N_pad=4), UNSUPPORTED), (dict(B=1 << 20, N_pad=1 << 12), INVALID),
+])
+def test_plan_create_rejects(lib, kw, want):
+    st, h = plan_create(lib, **kw)
+    assert st == want and h.value is None
+
+
+def test_plan_create_resolves_on_the_host_and_checks_pointers(lib):
+    st, h = plan_create(lib)
+    assert st == OK and h.value is not None
+    try:
+        assert lib.idx_plan_workspace_bytes(h) == lib.idx_workspace_bytes(4, 8192, 4, 256, 0)
+        ws = lib.idx_plan_workspace_bytes(h)
+        call = lambda **kw: lib.idx_plan_select(
+            kw.get("plan", h), kw.get("q", P), kw.get("c", P), kw.get("seq_len", P),
+            kw.get("ids", P), kw.get("counts", None), kw.get("scores_out", None),
+            kw.get("ws", P), kw.get("ws_bytes", ws), None)
+        assert call(plan=None) == INVALID
+        for k in ("q", "c", "seq_len", "ids"):
+            assert call(**{k: None}) == INVALID, k
+        assert call(q=P + 8) == INVALID and call(ids=P + 2) == INVALID
+        assert call(counts=P + 1) == INVALID and call(scores_out=P + 2) == INVALID
+        assert call(ws=None) == WORKSPACE and call(ws_bytes=ws - 1) == WORKSPACE
+        assert call(ws=P + 16) == WORKSPACE
+    finally:
+        lib.idx_plan_destroy(h)
+    lib.idx_plan_destroy(None)
+    assert lib.idx_plan_workspace_bytes(None) == 0
