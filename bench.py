@@ -929,7 +929,7 @@ def read_traffic(workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 11)))
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
