@@ -36,10 +36,12 @@ that call alone; isolated_empty_us is an empty launch timed the same way, the
 events' own overhead), host_e2e_us_per_call (host wall clock of one call plus a
 synchronise), sorted_us_per_call (score-ordered output where the headline is
 id-ordered), plan_host_e2e_us and plan_graph_host_e2e_us (the same through a
-resolved plan, and through a one-call graph of it), and floor (an empty
-launch, and a streaming read of the call's
-algorithmic bytes, alone and followed by one cross-workgroup arrival counter,
-timed like the call).
+resolved plan, and through a one-call graph of it), radix8_us_per_call (the
+same steps with IDX_RADIX8: four 8-bit radix passes and no linear-bin pass,
+timed like the headline; radix8_same_outputs must hold, or the run fails), and
+floor (an empty launch, and a streaming read of the call's algorithmic bytes,
+alone and followed by one cross-workgroup arrival counter, timed like the
+call).
 
 Other modes:
   --workload N         one workload only (1..10; 6: paged pool, 7: prompt tokens,
@@ -75,13 +77,14 @@ HEADLINE = 4
 DEFAULT_SET = (1, 2, 3, 4, 5, 9, 10)
 # empty launches with these workgroup counts bracket a workload's timed region
 MARK_BEGIN, MARK_END = 1000, 2000
+RADIX8_MARK = 50   # marker offset of a workload's IDX_RADIX8 region
 
 KERNEL = {1: "select_fused_kernel", 2: "select_fused_kernel", 3: "topk_split_kernel",
           4: "select_fused_kernel", 5: "assign_kernel", 6: "select_fused_kernel",
           7: "topk_kernel", 8: "pool_keys_kernel", 9: "topk_split_kernel", 10: "topk_kernel"}
 SOURCES = ["block_scoring_top_amd/csrc/" + f for f in
-           ("common.hpp", "score.hpp", "select.hpp", "indexer.hip", "assign.hip", "prefill.hip",
-            "pool.hip", "api.cpp")]
+           ("common.hpp", "score.hpp", "select.hpp", "indexer_kernels.hpp", "indexer.hip",
+            "indexer_radix8.hip", "assign.hip", "prefill.hip", "pool.hip", "api.cpp")]
 
 
 def source_digest() -> str:
@@ -132,6 +135,7 @@ def blas_threads():
 class Workload:
     unit = "blocks/s"
     sorted_variant = False      # headline id-ordered, score order reported beside it
+    radix8_variant = False      # the select with four 8-bit radix passes timed beside it
     dtype = "f32"
 
     def replicate(self, copies):
@@ -165,6 +169,7 @@ class Indexer(Workload):
         self.dtype = x.dtype
         self.inputs = [(to_dev(x.q), to_dev(x.c), to_dev(x.seq_len))]
         self.sorted_variant = not x.sorted
+        self.radix8_variant = True
         self.ids = torch.empty(x.B, x.K, dtype=torch.int32, device="cuda")
         self.counts = torch.empty(x.B, dtype=torch.int32, device="cuda")
         nbytes = idx.idx_workspace_bytes(x.B, x.N_pad, x.H, x.K, 0)
@@ -177,11 +182,11 @@ class Indexer(Workload):
         self.alg_bytes = self.units * x.D * elem + x.q.size * elem + 4 * x.B + 4 * x.B * x.K
         self.alg_flops = 2 * self.units * x.D  # after summing the heads once per request
 
-    def step(self, i, sorted=None):
+    def step(self, i, sorted=None, radix8=False):
         q, c, sl = self.inputs[i % len(self.inputs)]
         self.idx.idx_select(q, c, sl, self.x.K, page_size=self.x.page_size,
                             sorted=self.x.sorted if sorted is None else sorted,
-                            ids=self.ids, counts=self.counts, ws=self.ws)
+                            ids=self.ids, counts=self.counts, ws=self.ws, radix8=radix8)
 
     def out_tensors(self):
         return [self.ids, self.counts]
@@ -263,6 +268,7 @@ class Topk(Workload):
         self.x, self.torch, self.idx = x, torch, idx
         self.bf16 = x.scores.dtype == np.uint16   # bf16 rows go to idx_topk_bf16
         self.dtype = "bf16" if self.bf16 else "f32"
+        self.radix8_variant = not self.bf16
         self.inputs = [(to_dev(x.scores),)]
         B, N = x.scores.shape
         self.ids = torch.empty(B, x.K, dtype=torch.int32, device="cuda")
@@ -273,9 +279,9 @@ class Topk(Workload):
         self.alg_bytes = B * N * (2 if self.bf16 else 4) + B * x.K * 4
         self.alg_flops = 0
 
-    def step(self, i, sorted=None):
+    def step(self, i, sorted=None, radix8=False):
         self.idx.idx_topk(self.inputs[i % len(self.inputs)][0], self.x.K, None, bool(sorted),
-                          ids=self.ids, counts=self.counts, ws=self.ws)
+                          ids=self.ids, counts=self.counts, ws=self.ws, radix8=radix8)
 
     def out_tensors(self):
         return [self.ids, self.counts]
@@ -768,6 +774,22 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
             gs.replay()
             res["sorted_us_per_call"] = replay_ms(torch, gs, steps, flush) * 1e3
             del gs
+        if wl.radix8_variant:
+            # the same steps with four 8-bit radix passes (IDX_RADIX8): timed the
+            # same way, in a marked region, and its outputs must equal the
+            # headline's (which the CPU leg checks against the oracle)
+            import numpy as np
+            gr = capture(torch, lambda i: wl.step(i, radix8=True), steps)
+            gr.replay()
+            torch.cuda.synchronize()
+            wl.poison_outputs()
+            res["radix8_us_per_call"] = replay_ms(torch, gr, steps, flush, mark=RADIX8_MARK + wl.w,
+                                                  idx=idx) * 1e3
+            res["radix8_same_outputs"] = all(
+                np.array_equal(a, b) for a, b in zip(wl.timed_outputs(), outs))
+            del gr
+            log(f"[bench] w{wl.w} radix8: {res['radix8_us_per_call']:.2f} us per call, outputs "
+                f"{'equal' if res['radix8_same_outputs'] else 'DIFFERENT'}")
         res["floor"] = floors(torch, idx, wl, steps, flush)
         log(f"[bench] w{wl.w} floors: read {res['floor']['read_us']:.2f} us, read + hand-off "
             f"{res['floor']['read_handoff_us']:.2f} us, empty {res['floor']['empty_us']:.2f} us")
@@ -896,12 +918,13 @@ def parse_trace(d, out_path, command):
              "| workload | kernel | dispatches | average (us) | min (us) | max (us) |",
              "|---|---|---|---|---|---|"]
     for w in sorted(regions):
+        label = f"{w - RADIX8_MARK} (IDX_RADIX8)" if w > RADIX8_MARK else str(w)
         per = {}
         for r in regions[w]:
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             per.setdefault(r["Kernel_Name"].split("(")[0], []).append(dur)
         for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-            lines.append(f"| {w} | `{k}` | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} "
+            lines.append(f"| {label} | `{k}` | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} "
                          f"| {max(v):.2f} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -992,6 +1015,9 @@ def main():
                 log(f"[bench] w{w}: PARITY FAILED: {res['parity']['error']}")
         else:
             res["parity"] = {"ok": None, "note": "not checked (--no-cpu-baseline)"}
+        if res.get("radix8_same_outputs") is False:
+            failed.append(w)
+            log(f"[bench] w{w}: the IDX_RADIX8 select returned other outputs")
         res["dtype"] = wl.dtype
         results[w] = res
         del wl, outs
@@ -1013,7 +1039,8 @@ def main():
     }
     for k in ("parity", "cpu_baseline", "steady_us_per_call", "isolated_call_us",
               "isolated_empty_us", "host_e2e_us_per_call", "plan_host_e2e_us",
-              "plan_graph_host_e2e_us", "sorted_us_per_call", "floor",
+              "plan_graph_host_e2e_us", "sorted_us_per_call", "radix8_us_per_call",
+              "radix8_same_outputs", "floor",
               "input_copies", "distinct_read_bytes"):
         if k in h:
             out[k] = h[k]

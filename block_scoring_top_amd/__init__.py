@@ -16,7 +16,8 @@ import torch
 __all__ = ["idx_score", "idx_topk", "idx_topk_bf16", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
            "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
-           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IdxError",
+           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IDX_RADIX8",
+           "IdxError",
            "SelectPlan", "plan_for"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "libidx.so")
 
 IDX_F32, IDX_BF16 = 0, 1
 IDX_SORTED = 0x1
+IDX_RADIX8 = 0x2  # four 8-bit radix passes, no linear-bin pass (same results)
 IDX_CHUNK_SHIFT = 8
 
 _c_int, _c_size, _vp, _u32 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32
@@ -183,11 +185,13 @@ def idx_score(q, c, seq_len, page_size=16, scores=None):
     return scores
 
 
-def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None):
+def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None,
+             radix8=False):
     """Row-wise top-K indices (ties to the lower index), padded with -1. float32
-    scores go to idx_topk, bfloat16 ones to idx_topk_bf16."""
+    scores go to idx_topk, bfloat16 ones to idx_topk_bf16. radix8: the select
+    with four 8-bit radix passes (IDX_RADIX8; the same results)."""
     if scores.dtype == torch.bfloat16:
-        return idx_topk_bf16(scores, K, n_valid, sorted, ids, counts, ws)
+        return idx_topk_bf16(scores, K, n_valid, sorted, ids, counts, ws, radix8)
     lib = load()
     dev = _dev(scores, n_valid, ids, counts, ws)
     B, N = scores.shape
@@ -195,7 +199,7 @@ def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=No
         ids = torch.empty(B, K, dtype=torch.int32, device=dev)
     if counts is None:
         counts = torch.empty(B, dtype=torch.int32, device=dev)
-    flags = IDX_SORTED if sorted else 0
+    flags = (IDX_SORTED if sorted else 0) | (IDX_RADIX8 if radix8 else 0)
     nbytes = lib.idx_topk_workspace_bytes(B, N, K, flags)
     if ws is None and nbytes:
         ws = _workspace(dev, nbytes, "topk")
@@ -205,8 +209,10 @@ def idx_topk(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=No
     return ids, counts
 
 
-def idx_topk_bf16(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None):
-    """idx_topk over bfloat16 scores (16-bit keys, half the bytes read)."""
+def idx_topk_bf16(scores, K, n_valid=None, sorted=False, ids=None, counts=None, ws=None,
+                  radix8=False):
+    """idx_topk over bfloat16 scores (16-bit keys, half the bytes read). The
+    library rejects radix8 here (IDX_ERR_UNSUPPORTED)."""
     lib = load()
     dev = _dev(scores, n_valid, ids, counts, ws)
     if scores.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
@@ -216,7 +222,7 @@ def idx_topk_bf16(scores, K, n_valid=None, sorted=False, ids=None, counts=None, 
         ids = torch.empty(B, K, dtype=torch.int32, device=dev)
     if counts is None:
         counts = torch.empty(B, dtype=torch.int32, device=dev)
-    flags = IDX_SORTED if sorted else 0
+    flags = (IDX_SORTED if sorted else 0) | (IDX_RADIX8 if radix8 else 0)
     nbytes = lib.idx_topk_workspace_bytes(B, N, K, flags)
     if ws is None and nbytes:
         ws = _workspace(dev, nbytes, "topk")
@@ -227,8 +233,10 @@ def idx_topk_bf16(scores, K, n_valid=None, sorted=False, ids=None, counts=None, 
 
 
 def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False, ids=None,
-               counts=None, scores_out=None, ws=None, chunk_log2=0):
-    """Fused score + mask + top-K. Returns (ids, counts, scores_out or None)."""
+               counts=None, scores_out=None, ws=None, chunk_log2=0, radix8=False):
+    """Fused score + mask + top-K. Returns (ids, counts, scores_out or None).
+    radix8: the select with four 8-bit radix passes (IDX_RADIX8; the same
+    results)."""
     lib = load()
     dev = _dev(q, c, seq_len, ids, counts, scores_out, ws)
     B, H, D = q.shape
@@ -239,7 +247,8 @@ def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False
         counts = torch.empty(B, dtype=torch.int32, device=dev)
     if return_scores and scores_out is None:
         scores_out = torch.empty(B, N_pad, dtype=torch.float32, device=dev)
-    flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+    flags = ((IDX_SORTED if sorted else 0) | (IDX_RADIX8 if radix8 else 0)
+             | (int(chunk_log2) << IDX_CHUNK_SHIFT))
     nbytes = lib.idx_workspace_bytes(B, N_pad, H, K, flags)
     if ws is None:
         ws = _workspace(dev, nbytes, "select")
@@ -250,7 +259,7 @@ def idx_select(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False
 
 
 def idx_select_noalloc(q, c, seq_len, K, page_size=16, sorted=False, return_scores=False,
-                       ids=None, counts=None, scores_out=None, chunk_log2=0):
+                       ids=None, counts=None, scores_out=None, chunk_log2=0, radix8=False):
     """idx_select without a workspace: the library's static per-GPU scratch holds
     the arrival counters and staging (calls on one GPU must not overlap).
     Returns (ids, counts, scores_out or None)."""
@@ -264,7 +273,8 @@ def idx_select_noalloc(q, c, seq_len, K, page_size=16, sorted=False, return_scor
         counts = torch.empty(B, dtype=torch.int32, device=dev)
     if return_scores and scores_out is None:
         scores_out = torch.empty(B, N_pad, dtype=torch.float32, device=dev)
-    flags = (IDX_SORTED if sorted else 0) | (int(chunk_log2) << IDX_CHUNK_SHIFT)
+    flags = ((IDX_SORTED if sorted else 0) | (IDX_RADIX8 if radix8 else 0)
+             | (int(chunk_log2) << IDX_CHUNK_SHIFT))
     _check("idx_select_noalloc", lib.idx_select_noalloc(
         _ptr(q), _ptr(c), _ptr(seq_len), _ptr(ids), _ptr(counts), _ptr(scores_out), B, H, D,
         N_pad, page_size, K, _dtype_code(q), flags, _stream(dev)))

@@ -22,7 +22,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-I", os.path.join(ROOT, "include")]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
 
-HIP_SOURCES = ["indexer.hip", "assign.hip", "prefill.hip", "pool.hip", "floor.hip"]
+HIP_SOURCES = ["indexer.hip", "indexer_radix8.hip", "assign.hip", "prefill.hip", "pool.hip",
+               "floor.hip"]
 # assign.hip's inputs are finite by contract; without NaN semantics its running
 # max compiles to plain 3-input maxes (no per-operand canonicalisation)
 EXTRA_FLAGS = {"assign.hip": ["-fno-honor-nans"]}
@@ -46,7 +47,7 @@ def build(verbose: bool = False) -> str:
     for s in CXX_SOURCES:
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s),
                      "-o", os.path.join(BUILD, s + ".o")])
-    with ThreadPoolExecutor(max_workers=4) as ex:
+    with ThreadPoolExecutor(max_workers=6) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:

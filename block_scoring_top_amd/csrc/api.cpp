@@ -44,7 +44,7 @@ constexpr int kWideChunkMin = 32, kWideTarget = 256;
 int check_chunk_flag(uint32_t flags) {
   const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
   if (l != 0 && (l < 4 || l > 14)) return IDX_ERR_INVALID_ARG;
-  if (flags & ~(IDX_SORTED | IDX_CHUNK_MASK)) return IDX_ERR_INVALID_ARG;
+  if (flags & ~(IDX_SORTED | IDX_RADIX8 | IDX_CHUNK_MASK)) return IDX_ERR_INVALID_ARG;
   return IDX_OK;
 }
 
@@ -116,7 +116,8 @@ int topk_checked(const void* scores, bool bf16, const int32_t* n_valid, int32_t*
       !aligned(counts, 4))
     return IDX_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || K < 1) return IDX_ERR_INVALID_ARG;
-  if (flags & ~IDX_SORTED) return IDX_ERR_INVALID_ARG;
+  if (flags & ~(IDX_SORTED | IDX_RADIX8)) return IDX_ERR_INVALID_ARG;
+  if (bf16 && (flags & IDX_RADIX8) != 0) return IDX_ERR_UNSUPPORTED;
   if ((int64_t)B * N > (int64_t(1) << 40) || (int64_t)B * K > kMaxRows) return IDX_ERR_INVALID_ARG;
   const bool sorted = (flags & IDX_SORTED) != 0;
   if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
@@ -124,7 +125,8 @@ int topk_checked(const void* scores, bool bf16, const int32_t* n_valid, int32_t*
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
     return IDX_ERR_WORKSPACE;
   return hip_status(idxk::launch_topk(scores, n_valid, ids, counts, B, N, K, sorted,
-                                      need > 0 ? ws : nullptr, stream, false, bf16));
+                                      need > 0 ? ws : nullptr, stream, false, bf16,
+                                      (flags & IDX_RADIX8) != 0));
 }
 
 }  // namespace
@@ -195,6 +197,7 @@ struct SelectLaunch {
   int B, H, N_pad, page_size, K;
   bool bf16, sorted, wide;
   int chunk;
+  bool radix8;
 };
 
 SelectLaunch resolve_select(int B, int H, int N_pad, int page_size, int K, idx_dtype dt,
@@ -203,7 +206,8 @@ SelectLaunch resolve_select(int B, int H, int N_pad, int page_size, int K, idx_d
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
   const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
-  return SelectLaunch{B, H, N_pad, page_size, K, dt == IDX_BF16, sorted, wide, chunk};
+  return SelectLaunch{B,     H,      N_pad, page_size, K, dt == IDX_BF16, sorted, wide, chunk,
+                      (flags & IDX_RADIX8) != 0};
 }
 
 int launch_resolved(const SelectLaunch& L, const void* q, const void* c, const int32_t* seq_len,
@@ -212,7 +216,7 @@ int launch_resolved(const SelectLaunch& L, const void* q, const void* c, const i
   return hip_status(idxk::launch_select(q, c, seq_len, ids, counts, scores_out, L.B, L.H,
                                         L.N_pad, L.page_size, L.K, L.bf16, L.sorted, L.chunk,
                                         L.wide, tickets, stage, stage_stride(L.N_pad), nullptr,
-                                        nullptr, 0, 0, stream));
+                                        nullptr, 0, 0, stream, L.radix8));
 }
 
 int dispatch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
@@ -320,6 +324,7 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
   if (H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
   int st;
   if ((st = check_chunk_flag(flags)) != IDX_OK) return st;
+  if ((flags & IDX_RADIX8) != 0) return IDX_ERR_UNSUPPORTED;
   if (B > kMaxRequests) return IDX_ERR_UNSUPPORTED;
   const bool sorted = (flags & IDX_SORTED) != 0;
   if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
@@ -367,7 +372,8 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
   if (B < 1 || T < 1 || H < 1 || D < 1 || N_pad < 1 || page_size < 1 || K < 1)
     return IDX_ERR_INVALID_ARG;
   if (dt != IDX_F32 && dt != IDX_BF16) return IDX_ERR_INVALID_ARG;
-  if (flags & ~IDX_SORTED) return IDX_ERR_INVALID_ARG;
+  if (flags & ~(IDX_SORTED | IDX_RADIX8)) return IDX_ERR_INVALID_ARG;
+  if ((flags & IDX_RADIX8) != 0) return IDX_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)B * T;
   if (rows > kMaxRows || rows * N_pad > (int64_t(1) << 40) || rows * K > kMaxRows ||
       (int64_t)B * N_pad > kMaxRows)

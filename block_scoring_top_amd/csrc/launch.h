@@ -18,22 +18,33 @@ int launch_score(const void* q, const void* c, const int32_t* seq_len, float* sc
 // rows up to 8192 entries); otherwise rows of any distribution (bins chosen
 // per row).
 // bf16: the scores are bf16 (raw 16-bit patterns, any distribution).
+// radix8: fp32 rows selected with four 8-bit radix passes and no linear-bin
+// pass (the same results; for comparison).
 int launch_topk(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
                 int B, int N, int K, bool sorted, void* split_ws, void* stream,
-                bool dot_scores = false, bool bf16 = false);
+                bool dot_scores = false, bool bf16 = false, bool radix8 = false);
 int launch_topk_bf16(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
                      int B, int N, int K, bool sorted, void* split_ws, void* stream);
+int launch_topk_radix8(const void* scores, const int32_t* n_valid, int32_t* ids, int32_t* counts,
+                       int B, int N, int K, bool sorted, void* split_ws, void* stream,
+                       bool dot_scores);
 size_t topk_split_workspace_bytes(int B, int N, int K);
 
 // indptr == nullptr: dense tables (c is [B, N_pad, 128], seq_len gives the
 // valid rows). Otherwise paged: c is a pool of n_rows centroids, request b's
 // slots are indices[indptr[b] .. indptr[b+1]) (n_indices entries exist), N_pad
 // is the longest page list, and seq_len / page_size are unused.
+// radix8 (dense tables only): four 8-bit radix passes, no linear-bin pass.
 int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
                   int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
                   int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
                   float* stage, int stage_stride, const int32_t* indptr, const int32_t* indices,
-                  int64_t n_indices, int n_rows, void* stream);
+                  int64_t n_indices, int n_rows, void* stream, bool radix8 = false);
+int launch_select_radix8(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
+                         int32_t* counts, float* scores_out, int B, int H, int N_pad,
+                         int page_size, int K, bool bf16, bool sorted, int chunk, bool wide,
+                         uint32_t* tickets, float* stage, int stage_stride, const int32_t* indptr,
+                         const int32_t* indices, int64_t n_indices, int n_rows, void* stream);
 
 // The calling device's copy of the static scratch of idx_select_noalloc
 // (IDX_NOALLOC_SCRATCH_BYTES). The first call on a device looks up its address

@@ -51,20 +51,28 @@ constexpr int kMaxSortedK = 4096;
 constexpr bool kRefineBitonic = true;
 
 // Radix digits of the order keys. 32-bit keys: 11 + 11 + 10 bits. Keys of
-// bf16 scores (KEY16) carry only 16 bits of information: the low half of the
-// fp32 pattern is zero, so the low half of the key is 0x0000 for non-negative
-// scores and 0xFFFF for negative ones; two digits of 11 + 5 bits resolve them
-// ("Iterate Topk", section 6: a 16-bit radix for the bottom-zero bf16 keys).
-constexpr int kPasses = 3;  // the most passes of any key width (and "key resolved")
-template <bool KEY16>
-__device__ __forceinline__ int n_passes() { return KEY16 ? 2 : 3; }
-template <bool KEY16>
-__device__ __forceinline__ int digit_shift(int p) {
-  return p == 0 ? kDigit0Shift : (KEY16 ? 16 : (p == 1 ? 10 : 0));
+// bf16 scores (kDigits16) carry only 16 bits of information: the low half of
+// the fp32 pattern is zero, so the low half of the key is 0x0000 for
+// non-negative scores and 0xFFFF for negative ones; two digits of 11 + 5 bits
+// resolve them ("Iterate Topk", section 6: a 16-bit radix for the bottom-zero
+// bf16 keys). kDigits8: four 8-bit digits, the radix of the proposal seed in
+// "Iterate Topk" (section 6) and of the four-pass loop in "Round 18 Track C"
+// (section 1, Target 1), kept for comparison.
+enum DigitScheme : int { kDigits11 = 0, kDigits16 = 1, kDigits8 = 2 };
+constexpr int kResolved = 4;  // a `level` above every scheme's pass count: the whole key
+template <int DS>
+__device__ __forceinline__ int n_passes() {
+  return DS == kDigits8 ? 4 : (DS == kDigits16 ? 2 : 3);
 }
-template <bool KEY16>
+template <int DS>
+__device__ __forceinline__ int digit_shift(int p) {
+  if (DS == kDigits8) return 24 - 8 * p;
+  return p == 0 ? kDigit0Shift : (DS == kDigits16 ? 16 : (p == 1 ? 10 : 0));
+}
+template <int DS>
 __device__ __forceinline__ int digit_bits(int p) {
-  return p == 0 ? 11 : (KEY16 ? 5 : (p == 1 ? 11 : 10));
+  if (DS == kDigits8) return 8;
+  return p == 0 ? 11 : (DS == kDigits16 ? 5 : (p == 1 ? 11 : 10));
 }
 // the whole key of a bf16 score from its 16 significant bits
 __device__ __forceinline__ uint32_t key16_full(uint32_t top) {
@@ -735,9 +743,11 @@ __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uin
 // striped row chooses value or key bins from the mean of its scores.
 // BF16IN: the row holds bf16 scores (striped rows only). KEY16: every key is
 // that of a bf16 score (bf16 rows, or candidates taken from them), so two
-// radix digits resolve a key.
+// radix digits resolve a key. RADIX8: four 8-bit radix passes, no linear-bin
+// pass (the same results, for comparison).
 template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut,
-          bool ADAPTIVE = (!BLOCKED && SLOTS >= 8), bool BF16IN = false, bool KEY16 = BF16IN>
+          bool ADAPTIVE = (!BLOCKED && SLOTS >= 8), bool BF16IN = false, bool KEY16 = BF16IN,
+          bool RADIX8 = false>
 __device__ __attribute__((always_inline)) void select_row(const void* row, int n, int cap, int K,
                                                          const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
@@ -748,6 +758,9 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
   static_assert(NT >= 256 && NT <= 1024 && NT % 256 == 0,
                 "256 to 1024 threads: the bin search gives each thread 2 to 8 bins");
   static_assert(!(BF16IN && BLOCKED), "bf16 rows use the striped layout");
+  static_assert(!(RADIX8 && KEY16), "8-bit digits are built for 32-bit keys only");
+  // RADIX8: four 8-bit radix passes and no linear-bin pass (for comparison)
+  constexpr int kDS = RADIX8 ? kDigits8 : (KEY16 ? kDigits16 : kDigits11);
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & (kWave - 1);
@@ -789,7 +802,7 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
   // (rows longer than one tile of the fused select, held in registers only
   // when a request is shorter than its table).
   constexpr bool kAdaptive = ADAPTIVE && !BLOCKED;
-  constexpr bool kLinear = BLOCKED || SLOTS <= 2 || kAdaptive;
+  constexpr bool kLinear = (BLOCKED || SLOTS <= 2 || kAdaptive) && !RADIX8;
   const bool upfront = kLinear && cached;  // the range is taken before the passes
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   if (upfront) {
@@ -829,7 +842,7 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
   __syncthreads();
 
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
-  int level = 0;  // digits resolved (kPasses = the whole key)
+  int level = 0;  // digits resolved (kResolved = the whole key)
   bool take_all = false, resolved = false;
   // simple threshold: exactly the keys whose class value (the key, or its
   // linear bin) is at least t_lo are taken, with no partial tie
@@ -987,7 +1000,7 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
         __syncthreads();
         prefix = sm.same_key;
         need = sm.sel_need;
-        level = kPasses;
+        level = kResolved;
         resolved = true;
         if (sm.all_same) {
           simple = true;
@@ -1018,13 +1031,13 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
         if (sm.same_key == sm.bin_max) {
           prefix = sm.same_key;
           need = bneed;
-          level = kPasses;
+          level = kResolved;
           resolved = true;
         } else if (kRefineBitonic && btot <= (uint32_t)refine_cap<NT>()) {
           uint32_t neq;
           prefix = refine_bin_bitonic<NT, SLOTS>(keys, bins, sb, btot, bneed, sm, slot_live, &neq);
           need = neq;
-          level = kPasses;
+          level = kResolved;
           resolved = true;
         } else {
           // the linear counts are in histogram 0 and histogram 1 is clear, or
@@ -1038,12 +1051,12 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
   // Each pass histograms the next digit of the keys that still match the
   // resolved prefix, then finds the bin holding the need-th largest of them
   // (wave 0, find_bin above).
-  for (int p = 0; p < (resolved ? 0 : n_passes<KEY16>()); ++p) {
+  for (int p = 0; p < (resolved ? 0 : n_passes<kDS>()); ++p) {
     const int buf = (p + boff) & 1;
     uint32_t* h = sm.hist[buf];
-    const int shift = digit_shift<KEY16>(p);
-    const uint32_t dmask = (1u << digit_bits<KEY16>(p)) - 1u;
-    const int hshift = p == 0 ? 0 : digit_shift<KEY16>(p - 1);  // the resolved bits sit above this
+    const int shift = digit_shift<kDS>(p);
+    const uint32_t dmask = (1u << digit_bits<kDS>(p)) - 1u;
+    const int hshift = p == 0 ? 0 : digit_shift<kDS>(p - 1);  // the resolved bits sit above this
     // this pass takes the range of its keys
     const bool track = (p == 0 && !upfront) || (!BLOCKED && p == 1);
     if (p == 1) {
@@ -1101,19 +1114,19 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
     // `need` are taken (identical keys would only fill one bin per later pass)
     if ((p == 0 || (!BLOCKED && p == 1)) && sm.all_same) {
       prefix = sm.same_key;
-      level = kPasses;
+      level = kResolved;
       break;
     }
-    prefix = (prefix << digit_bits<KEY16>(p)) | sm.sel_bin;
+    prefix = (prefix << digit_bits<kDS>(p)) | sm.sel_bin;
     need = sm.sel_need;
     level = p + 1;
     if (KEY16 && p == 1) {  // the 16 significant bits fix the whole key
       prefix = key16_full(prefix);
-      level = kPasses;
+      level = kResolved;
     }
     if (sm.sel_tot == need) {  // the whole bin is taken: every key from its lowest on
       simple = true;
-      t_lo = level == kPasses ? prefix : prefix << digit_shift<KEY16>(p);
+      t_lo = level == kResolved ? prefix : prefix << digit_shift<kDS>(p);
       break;
     }
   }
@@ -1128,7 +1141,8 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
     simple = true;
     t_lo = kKeyNegInf + 1u;
   }
-  const int shiftL = level == 1 ? kDigit0Shift : (level == 2 ? 10 : 0);  // (KEY16: 1 or kPasses)
+  // the bits below the resolved digits (KEY16 rows: level 1 or kResolved)
+  const int shiftL = (level <= 0 || level >= kResolved) ? 0 : digit_shift<kDS>(level - 1);
   const uint32_t lo_b = simple ? t_lo : prefix << shiftL;
   const uint32_t hi_b = simple ? t_lo - 1u : lo_b | ((1u << shiftL) - 1u);
   const uint32_t need_e = simple ? 0u : need;

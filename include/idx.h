@@ -65,6 +65,15 @@ enum {
 /* flags */
 #define IDX_SORTED 0x1u /* ids ordered by (score descending, id ascending);
                            default: ascending block id                        */
+/* IDX_RADIX8: find the threshold with four 8-bit radix passes and no
+ * linear-bin pass: the radix of the proposal seed in [TK] section 6 and of the
+ * four-pass select loop in [QS] section 1 Target 1. The outputs are the same
+ * as without it (same selection rule, same order); it exists to measure that
+ * design against the library's own select (a linear-bin pass, then 11 + 11 +
+ * 10-bit digits). Accepted by idx_topk (fp32 scores), idx_select,
+ * idx_select_noalloc and idx_plan_create; idx_topk_bf16, idx_select_paged and
+ * idx_select_prefill return IDX_ERR_UNSUPPORTED for it. */
+#define IDX_RADIX8 0x2u
 /* Bits 8..12 of `flags` optionally fix log2 of the number of blocks scored by
  * one workgroup (4..14); 0 lets the library choose. Results do not depend on it. */
 #define IDX_CHUNK_SHIFT 8

@@ -134,6 +134,7 @@ def topk_bf16_call(lib, **kw):
     (dict(scores=P + 2), INVALID), (dict(ids=P + 2), INVALID), (dict(n_valid=P + 1), INVALID),
     (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(K=0), INVALID), (dict(flags=0x80), INVALID),
     (dict(K=4097, flags=1), UNSUPPORTED), (dict(B=64, N=30000, K=2048), WORKSPACE),
+    (dict(flags=2), UNSUPPORTED),            # IDX_RADIX8: 32-bit keys only
 ])
 def test_topk_bf16_rejects(lib, kw, want):
     assert topk_bf16_call(lib, **kw) == want
@@ -209,6 +210,7 @@ def paged_call(lib, **kw):
     (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
     (dict(B=16385, max_pages=4), UNSUPPORTED), (dict(ws=None), WORKSPACE),
     (dict(ws=P, ws_bytes=100), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
+    (dict(flags=2), UNSUPPORTED),            # IDX_RADIX8: dense tables only
 ])
 def test_select_paged_rejects(lib, kw, want):
     assert paged_call(lib, **kw) == want
@@ -238,6 +240,7 @@ def prefill_call(lib, **kw):
     (dict(dt=3), INVALID), (dict(flags=0x100), INVALID), (dict(dt=0), UNSUPPORTED),
     (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(ws=P, ws_bytes=64), WORKSPACE), (dict(ws=P + 64), WORKSPACE),
+    (dict(flags=2), UNSUPPORTED), (dict(flags=3), UNSUPPORTED),  # IDX_RADIX8
 ])
 def test_select_prefill_rejects(lib, kw, want):
     assert prefill_call(lib, **kw) == want
@@ -349,3 +352,12 @@ def test_plan_create_resolves_on_the_host_and_checks_pointers(lib):
         lib.idx_plan_destroy(h)
     lib.idx_plan_destroy(None)
     assert lib.idx_plan_workspace_bytes(None) == 0
+
+
+def test_radix8_flag_in_the_header_and_accepted_by_a_plan(lib):
+    src = open(os.path.join(ROOT, "include", "idx.h")).read()
+    assert "#define IDX_RADIX8 0x2u" in src
+    for flags in (2, 3):
+        st, h = plan_create(lib, flags=flags)
+        assert st == OK and h.value is not None
+        lib.idx_plan_destroy(h)
