@@ -11,12 +11,19 @@
 // the argmax is a running max in registers: the score matrix is never written.
 //
 // Layout: the MFMA's A operand is a 32-centroid x 16-dim slice of C (from a
-// double-buffered LDS tile of 64 centroids, filled by direct-to-LDS loads that
-// overlap the previous tile's products), the B operand a 16-dim x 32-point
-// slice of X^T (registers, loaded once). The 32x32 result tile then has one
-// point per lane column (lane % 32) and 16 centroid rows per lane, so the max
-// over centroids is mostly in-lane; lanes l and l^32 hold disjoint centroid rows
-// of the same point and are merged once at the end.
+// triple-buffered LDS tile of 64 centroids, filled by direct-to-LDS loads that
+// overlap the products of the tiles before it), the B operand a 16-dim x
+// 32-point slice of X^T (registers, loaded once). The 32x32 result tile then
+// has one point per lane column (lane % 32) and 16 centroid rows per lane, so
+// the max over centroids is mostly in-lane; lanes l and l^32 hold disjoint
+// centroid rows of the same point and are merged once at the end.
+//
+// Software pipeline: two accumulator sets alternate between tiles. While the
+// products of tile t accumulate into one set, the running argmax of tile t-1
+// is taken from the other, a quarter of an accumulator per k-step, so that its
+// vector instructions issue in the shadow of that k-step's matrix products
+// (each k-step is a scheduling region of its own; it also reads the next
+// k-step's A fragments from LDS).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -67,10 +74,11 @@ __device__ __forceinline__ int swz(int r, int k) { return r * kChunks + (k ^ (r 
 // Load i of wave w fills the 64 consecutive 16-byte LDS slots p = 64 (4w + i) +
 // lane; slot p holds chunk (p & 15) ^ (row & 15) of tile row p >> 4, which is
 // the swizzled layout the MFMA operand reads expect. Rows past C repeat row C-1
-// (their bias is -inf, so they never win). Each wave also brings 16 of the
-// tile's biases from the -inf-padded norm buffer, so every wave issues the same
-// kLoadsPerTile loads per tile.
-constexpr int kBiasPerWave = kAsgTileC / (kAsgNT / kWave);
+// (their bias is -inf, so they never win). Each wave also writes all 64 of the
+// tile's biases (the same values in every wave, from the -inf-padded norm
+// buffer), so every wave issues the same kLoadsPerTile loads per tile and none
+// branches. A tile past the last one (loaded by the pipeline's last steps and
+// never read) takes its rows from row C-1 and its biases from the last tile.
 constexpr int kLoadsPerTile = kTileLoads + 1;
 __device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
                                                const float* __restrict__ cn, int C, int j0,
@@ -86,9 +94,8 @@ __device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
     const int j = j0 + row < C ? j0 + row : C - 1;
     __builtin_amdgcn_global_load_lds(c + (size_t)j * kHeadDim + k * 8, tile + slot0, 16, 0, 0);
   }
-  if (lane < kBiasPerWave)
-    __builtin_amdgcn_global_load_lds(cn + j0 + w * kBiasPerWave + lane, tn + w * kBiasPerWave, 4,
-                                     0, 0);
+  const int jb = min(j0, (C - 1) / kAsgTileC * kAsgTileC);
+  __builtin_amdgcn_global_load_lds(cn + jb + lane, tn, 4, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory count (expcnt and lgkmcnt left at
@@ -114,89 +121,100 @@ struct ArgmaxState {
   int bidx[kCB];
 };
 
-// One centroid tile: A fragments and biases from LDS tile `cur`, then (once
-// they are in registers) the direct-to-LDS load of tile `tile + 2` into `nxt`,
-// the products, the running argmax, and the wait for tile `tile + 1`.
-__device__ __forceinline__ void assign_tile(const uint16_t* __restrict__ c,
-                                            const float* __restrict__ cn, int C, int tile,
-                                            int ntiles, const uint4* cur, const float4* curn,
-                                            uint4* nxt, float* nxtn, const uint4 (&xb)[kCB][8],
-                                            ArgmaxState& st) {
+// Running argmax of one 32x32 accumulator tile, without branches: the lane's
+// 16 rows are centroids jbase + 8 (r >> 2) + (r & 3), r = 0..15 (jbase
+// includes the lane's 4 * half). Part 0 takes the max m and searches rows
+// 15..8 for it, part 1 searches rows 7..0 and updates the running best. The
+// search keeps the lowest row holding m, and a strictly larger m replaces the
+// best, so among equal values the lowest centroid index wins (tiles and row
+// blocks are visited in increasing index order).
+__device__ __forceinline__ void argmax_part0(const f32x16& v, float& m, int& rr) {
+  m = v[0];
+#pragma unroll
+  for (int r = 1; r < 15; r += 2)  // a chain of 3-input maxes
+    m = __builtin_fmaxf(__builtin_fmaxf(m, v[r]), v[r + 1]);
+  m = __builtin_fmaxf(m, v[15]);
+  rr = 8 * 3 + 3;  // the row offset of r = 15
+#pragma unroll
+  for (int r = 14; r >= 8; --r) rr = (v[r] == m) ? (8 * (r >> 2) + (r & 3)) : rr;
+}
+__device__ __forceinline__ void argmax_part1(const f32x16& v, float m, int rr, int jbase,
+                                             float& best, int& bidx) {
+#pragma unroll
+  for (int r = 7; r >= 0; --r) rr = (v[r] == m) ? (8 * (r >> 2) + (r & 3)) : rr;
+  const bool better = m > best;
+  best = better ? m : best;
+  bidx = better ? jbase + rr : bidx;
+}
+
+// One tile step: the products of tile `tile` (LDS tile cur) into accumulator
+// set `acc`, the direct-to-LDS refill of tile + 2 into nxt (the tile read two
+// steps ago, which every wave has finished: the previous step ended with a
+// barrier), and, with EPI, the argmax of the previous tile from `prev`,
+// interleaved with the products. aoff[ks] is the byte offset of this lane's A
+// fragment of k-step ks within a tile (the second 32-row block is 8 KiB on).
+template <bool EPI>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ c,
+                                          const float* __restrict__ cn, int C, int tile,
+                                          const uint4* cur, const float4* curn, uint4* nxt,
+                                          float* nxtn, const uint4 (&xb)[kCB][8],
+                                          f32x16 (&acc)[2][kCB], const f32x16 (&prev)[2][kCB],
+                                          ArgmaxState& st, const int (&aoff)[8]) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int col = lane & 31;
   const int half = lane >> 5;
   const int j0 = tile * kAsgTileC;
-  bf16x8 a[8][2];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    a[ks][0] = as_bf16x8(cur[swz(col, 2 * ks + half)]);
-    a[ks][1] = as_bf16x8(cur[swz(32 + col, 2 * ks + half)]);
-  }
-  float4 bias[2][4];  // rows 8g + 4*half + 0..3 of 32-row block rb
+  const char* curb = reinterpret_cast<const char*>(cur);
+  auto afrag = [&](int ks, int rb) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(curb + aoff[ks] + rb * 32 * kChunks * 16));
+  };
+  // The biases (rows 8g + 4 half + 0..3 of each 32-row block) go straight into
+  // the last point block's accumulators: the first k-step's products of every
+  // point block start from them.
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) bias[rb][g] = curn[rb * 8 + 2 * g + half];
-  const bool refill = tile + 2 < ntiles;
-  if (refill) load_ctile_lds(c, cn, C, j0 + 2 * kAsgTileC, nxt, nxtn);
-
-  // independent accumulator chains: 2 centroid blocks x kCB point blocks
-  f32x16 acc[2][kCB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        acc[rb][cb][4 * g + 0] = bias[rb][g].x;
-        acc[rb][cb][4 * g + 1] = bias[rb][g].y;
-        acc[rb][cb][4 * g + 2] = bias[rb][g].z;
-        acc[rb][cb][4 * g + 3] = bias[rb][g].w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const float4 b4 = curn[rb * 8 + 2 * g + half];
+      acc[rb][kCB - 1][4 * g + 0] = b4.x;
+      acc[rb][kCB - 1][4 * g + 1] = b4.y;
+      acc[rb][kCB - 1][4 * g + 2] = b4.z;
+      acc[rb][kCB - 1][4 * g + 3] = b4.w;
     }
-  }
+  bf16x8 a0 = afrag(0, 0);
+  bf16x8 a1 = afrag(0, 1);
+  load_ctile_lds(c, cn, C, j0 + 2 * kAsgTileC, nxt, nxtn);
+  __builtin_amdgcn_sched_barrier(0);
+  const int jp = j0 - kAsgTileC + 4 * half;  // the previous tile's rows of this lane
+  float m = 0.f;
+  int rr = 0;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 n0 = a0, n1 = a1;
+    if (ks < 7) {  // the next k-step's fragments
+      n0 = afrag(ks + 1, 0);
+      n1 = afrag(ks + 1, 1);
+    }
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       const bf16x8 b = as_bf16x8(xb[cb][ks]);
-      acc[0][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][0], b, acc[0][cb], 0, 0, 0);
-      acc[1][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][1], b, acc[1][cb], 0, 0, 0);
+      acc[0][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a0, b, ks == 0 ? acc[0][kCB - 1] : acc[0][cb], 0, 0, 0);
+      acc[1][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a1, b, ks == 0 ? acc[1][kCB - 1] : acc[1][cb], 0, 0, 0);
     }
-  }
-  // Running argmax. The 16 values of a lane are reduced with 3-input maxes;
-  // only when some lane of the wave finds a strictly larger value is the index
-  // of its first (lowest-index) occurrence searched. For a fixed lane the
-  // centroid index increases with (tile, rb, r), so strict comparisons keep
-  // the lowest index among equal values.
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      const f32x16& v = acc[rb][cb];
-      float m = v[0];
-#pragma unroll
-      for (int r = 1; r < 15; r += 2)  // a chain of 3-input maxes
-        m = __builtin_fmaxf(__builtin_fmaxf(m, v[r]), v[r + 1]);
-      m = __builtin_fmaxf(m, v[15]);
-      const bool better = m > st.best[cb];
-      if (__builtin_amdgcn_ballot_w64(better) != 0) {
-        int rr = 15;
-#pragma unroll
-        for (int r = 14; r >= 0; --r) rr = (v[r] == m) ? r : rr;
-        if (better) {
-          st.best[cb] = m;
-          st.bidx[cb] = j0 + rb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
-        }
-      }
+    if constexpr (EPI) {  // k-steps 2i, 2i+1: accumulator (cb, rb) = (i >> 1, i & 1)
+      const int cb = ks >> 2, rb = (ks >> 1) & 1;
+      if ((ks & 1) == 0) argmax_part0(prev[rb][cb], m, rr);
+      else argmax_part1(prev[rb][cb], m, rr, jp + 32 * rb, st.best[cb], st.bidx[cb]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    a0 = n0;
+    a1 = n1;
   }
-  // Tile `tile + 1` has landed once at most the loads just issued for tile
-  // `tile + 2` are outstanding in this wave, and in every wave after the
-  // barrier; the barrier also frees `cur` for the refill issued next step.
-  // (A plain barrier: the fence of __syncthreads would wait for every load.)
-  if (refill) wait_vmcnt<kLoadsPerTile>();
-  else wait_vmcnt<0>();
+  // Tile + 1 has landed once at most this step's refill loads are outstanding
+  // in this wave, and in every wave after the barrier, which also frees `cur`
+  // for the next step's refill.
+  wait_vmcnt<kLoadsPerTile>();
   tile_barrier();
 }
 
@@ -206,8 +224,9 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
                                                            int32_t* __restrict__ assign,
                                                            float* __restrict__ best_out,
                                                            int64_t N, int C) {
-  // three LDS tiles of 64 centroids (16 KiB each) and their biases, as
-  // separate objects: tile t+2 streams in while tile t is multiplied
+  // three LDS tiles of 64 centroids (16 KiB each) and their biases, as separate
+  // objects: the compiler then tells a refill's target from the tile being
+  // read, and the reads do not wait for the refill
   __shared__ uint4 ct0[kAsgTileC * kChunks], ct1[kAsgTileC * kChunks], ct2[kAsgTileC * kChunks];
   __shared__ float4 cn0[kAsgTileC / 4], cn1[kAsgTileC / 4], cn2[kAsgTileC / 4];
   const int t = threadIdx.x;
@@ -234,27 +253,69 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
     st.best[cb] = -__builtin_inff();
     st.bidx[cb] = 0;
   }
+  // A fragment offsets, computed once (kept in registers: otherwise the
+  // compiler recomputes them per buffer and step, and spills)
+  int aoff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    aoff[ks] = swz(col, 2 * ks + half) * 16;
+    asm volatile("" : "+v"(aoff[ks]));
+  }
   const int ntiles = (C + kAsgTileC - 1) / kAsgTileC;
   load_ctile_lds(c, cn, C, 0, ct0, reinterpret_cast<float*>(cn0));
-  if (ntiles > 1) {
-    load_ctile_lds(c, cn, C, kAsgTileC, ct1, reinterpret_cast<float*>(cn1));
-    wait_vmcnt<kLoadsPerTile>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  load_ctile_lds(c, cn, C, kAsgTileC, ct1, reinterpret_cast<float*>(cn1));
+  wait_vmcnt<kLoadsPerTile>();
   tile_barrier();
 
-  // unrolled by three so that every LDS access names its buffer at compile time
-  for (int tile = 0; tile < ntiles; tile += 3) {
-    assign_tile(c, cn, C, tile, ntiles, ct0, cn0, ct2, reinterpret_cast<float*>(cn2), xb, st);
-    if (tile + 1 >= ntiles) break;
-    assign_tile(c, cn, C, tile + 1, ntiles, ct1, cn1, ct0, reinterpret_cast<float*>(cn0), xb, st);
-    if (tile + 2 >= ntiles) break;
-    assign_tile(c, cn, C, tile + 2, ntiles, ct2, cn2, ct1, reinterpret_cast<float*>(cn1), xb, st);
+  // Tile tl + PH uses LDS tile (tl + PH) % 3 and accumulator set (tl + PH) % 2:
+  // the loop is unrolled by six so that both are fixed at compile time.
+  f32x16 accA[2][kCB], accB[2][kCB];
+#define IDX_STEP(PH, EPI_, CUR, CURN, NXT, NXTN)                                              \
+  tile_step<EPI_>(c, cn, C, tl + (PH), CUR, CURN, NXT, reinterpret_cast<float*>(NXTN), xb,    \
+                  ((PH) % 2) ? accB : accA, ((PH) % 2) ? accA : accB, st, aoff)
+  int tl = 0;
+  IDX_STEP(0, false, ct0, cn0, ct2, cn2);
+  for (tl = 0; tl + 1 < ntiles; tl += 6) {
+    IDX_STEP(1, true, ct1, cn1, ct0, cn0);
+    if (tl + 2 >= ntiles) break;
+    IDX_STEP(2, true, ct2, cn2, ct1, cn1);
+    if (tl + 3 >= ntiles) break;
+    IDX_STEP(3, true, ct0, cn0, ct2, cn2);
+    if (tl + 4 >= ntiles) break;
+    IDX_STEP(4, true, ct1, cn1, ct0, cn0);
+    if (tl + 5 >= ntiles) break;
+    IDX_STEP(5, true, ct2, cn2, ct1, cn1);
+    if (tl + 6 >= ntiles) break;
+    IDX_STEP(6, true, ct0, cn0, ct2, cn2);
   }
+#undef IDX_STEP
+  // the last tile's argmax
+  {
+    const int last = ntiles - 1;
+    const int jp = last * kAsgTileC + 4 * half;
+    auto epi = [&](const f32x16 (&pa)[2][kCB]) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float m;
+          int rr;
+          argmax_part0(pa[rb][cb], m, rr);
+          argmax_part1(pa[rb][cb], m, rr, jp + 32 * rb, st.best[cb], st.bidx[cb]);
+        }
+    };
+    if (last & 1) epi(accB);
+    else epi(accA);
+  }
+  wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
   float* best = st.best;
   int* bidx = st.bidx;
 
+  // The point indices are derived again from an opaque copy of the thread
+  // index: kept from the start, they would hold registers across the loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int64_t q0 = (int64_t)blockIdx.x * kAsgPts + (tid >> 6) * kAsgPtsPerWave + (tid & 31);
   // merge the two lanes that share a point (l and l^32)
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
@@ -264,7 +325,7 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
       best[cb] = ov;
       bidx[cb] = oi;
     }
-    const int64_t p = p0 + cb * 32 + col;
+    const int64_t p = q0 + cb * 32;
     if (half == 0 && p < N) {
       assign[p] = bidx[cb];
       if (best_out != nullptr) best_out[p] = best[cb];

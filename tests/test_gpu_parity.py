@@ -298,7 +298,11 @@ def run_assign(xb, cb):
     return a.cpu().numpy(), best.cpu().numpy()
 
 
-@pytest.mark.parametrize("N,C", [(1, 1), (1000, 100), (4097, 1024), (3000, 1031)])
+# C covers 1 to 8, 16 and 17 tiles of 64 centroids (the tile loop is unrolled
+# by six and software-pipelined over two accumulator sets), whole and partial
+@pytest.mark.parametrize("N,C", [(1, 1), (700, 64), (700, 65), (1000, 100), (2000, 130),
+                                 (1800, 256), (1700, 300), (1500, 384), (900, 390),
+                                 (1500, 449), (4097, 1024), (3000, 1031)])
 def test_assign_small(N, C):
     x = synth.make_assign(N, C, 128, 500 + N)
     say(f"[assign] N={N} C={C}")
