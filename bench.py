@@ -734,8 +734,8 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
     dict (without the oracle side) and the host copies of the timed outputs."""
     import math
     copies = max(1, math.ceil(ROTATE_BYTES / wl.alg_bytes) + 1)
-    if steps is None:  # a workload beside the headline: every copy read, at least 12 steps
-        steps = max(copies, 12)
+    if steps is None:  # a workload beside the headline: every copy read, at least 32 steps
+        steps = max(copies, 32)
     copies = min(copies, steps)
     wl.replicate(copies)
     for i in range(warmup):

@@ -80,11 +80,34 @@ __device__ __forceinline__ int swz(int r, int k) { return r * kChunks + (k ^ (r 
 // branches. A tile past the last one (loaded by the pipeline's last steps and
 // never read) takes its rows from row C-1 and its biases from the last tile.
 constexpr int kLoadsPerTile = kTileLoads + 1;
-__device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
-                                               const float* __restrict__ cn, int C, int j0,
-                                               uint4* tile, float* tn) {
+// Byte offset of load i of this lane within a tile of whole rows.
+__device__ __forceinline__ int refill_off(int i) {
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & (kWave - 1);
+  const int p = (w * kTileLoads + i) * kWave + lane;
+  const int row = p >> 4;
+  const int k = (p & 15) ^ (row & 15);
+  return row * kHeadDim * 2 + k * 16;
+}
+// roff[i] = refill_off(i), computed once: a tile of 64 whole rows is loaded
+// from the tile's base plus these offsets; a partial last tile (and a tile
+// past the end) clamps each row to C - 1.
+__device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
+                                               const float* __restrict__ cn, int C, int j0,
+                                               uint4* tile, float* tn,
+                                               const int (&roff)[kTileLoads]) {
+  const int t = threadIdx.x;
+  const int w = t >> 6, lane = t & (kWave - 1);
+  const int jb = min(j0, (C - 1) / kAsgTileC * kAsgTileC);
+  if (j0 + kAsgTileC <= C) {
+    const char* base = reinterpret_cast<const char*>(c + (size_t)j0 * kHeadDim);
+#pragma unroll
+    for (int i = 0; i < kTileLoads; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(base + roff[i]),
+                                       tile + (w * kTileLoads + i) * kWave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(cn + jb + lane, tn, 4, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kTileLoads; ++i) {
     const int slot0 = (w * kTileLoads + i) * kWave;  // wave-uniform LDS base
@@ -94,7 +117,6 @@ __device__ __forceinline__ void load_ctile_lds(const uint16_t* __restrict__ c,
     const int j = j0 + row < C ? j0 + row : C - 1;
     __builtin_amdgcn_global_load_lds(c + (size_t)j * kHeadDim + k * 8, tile + slot0, 16, 0, 0);
   }
-  const int jb = min(j0, (C - 1) / kAsgTileC * kAsgTileC);
   __builtin_amdgcn_global_load_lds(cn + jb + lane, tn, 4, 0, 0);
 }
 
@@ -159,7 +181,8 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ c,
                                           const uint4* cur, const float4* curn, uint4* nxt,
                                           float* nxtn, const uint4 (&xb)[kCB][8],
                                           f32x16 (&acc)[2][kCB], const f32x16 (&prev)[2][kCB],
-                                          ArgmaxState& st, const int (&aoff)[8]) {
+                                          ArgmaxState& st, const int (&aoff)[8],
+                                          const int (&roff)[kTileLoads]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int half = lane >> 5;
   const int j0 = tile * kAsgTileC;
@@ -182,7 +205,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ c,
     }
   bf16x8 a0 = afrag(0, 0);
   bf16x8 a1 = afrag(0, 1);
-  load_ctile_lds(c, cn, C, j0 + 2 * kAsgTileC, nxt, nxtn);
+  load_ctile_lds(c, cn, C, j0 + 2 * kAsgTileC, nxt, nxtn, roff);
   __builtin_amdgcn_sched_barrier(0);
   const int jp = j0 - kAsgTileC + 4 * half;  // the previous tile's rows of this lane
   float m = 0.f;
@@ -253,17 +276,23 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
     st.best[cb] = -__builtin_inff();
     st.bidx[cb] = 0;
   }
-  // A fragment offsets, computed once (kept in registers: otherwise the
-  // compiler recomputes them per buffer and step, and spills)
+  // A fragment and refill offsets, computed once and kept opaque (otherwise
+  // the compiler recomputes them per buffer and step, and spills)
   int aoff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     aoff[ks] = swz(col, 2 * ks + half) * 16;
     asm volatile("" : "+v"(aoff[ks]));
   }
+  int roff[kTileLoads];
+#pragma unroll
+  for (int i = 0; i < kTileLoads; ++i) {
+    roff[i] = refill_off(i);
+    asm volatile("" : "+v"(roff[i]));
+  }
   const int ntiles = (C + kAsgTileC - 1) / kAsgTileC;
-  load_ctile_lds(c, cn, C, 0, ct0, reinterpret_cast<float*>(cn0));
-  load_ctile_lds(c, cn, C, kAsgTileC, ct1, reinterpret_cast<float*>(cn1));
+  load_ctile_lds(c, cn, C, 0, ct0, reinterpret_cast<float*>(cn0), roff);
+  load_ctile_lds(c, cn, C, kAsgTileC, ct1, reinterpret_cast<float*>(cn1), roff);
   wait_vmcnt<kLoadsPerTile>();
   tile_barrier();
 
@@ -272,7 +301,7 @@ __global__ __launch_bounds__(kAsgNT, 2) void assign_kernel(const uint16_t* __res
   f32x16 accA[2][kCB], accB[2][kCB];
 #define IDX_STEP(PH, EPI_, CUR, CURN, NXT, NXTN)                                              \
   tile_step<EPI_>(c, cn, C, tl + (PH), CUR, CURN, NXT, reinterpret_cast<float*>(NXTN), xb,    \
-                  ((PH) % 2) ? accB : accA, ((PH) % 2) ? accA : accB, st, aoff)
+                  ((PH) % 2) ? accB : accA, ((PH) % 2) ? accA : accB, st, aoff, roff)
   int tl = 0;
   IDX_STEP(0, false, ct0, cn0, ct2, cn2);
   for (tl = 0; tl + 1 < ntiles; tl += 6) {
