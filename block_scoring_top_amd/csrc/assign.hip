@@ -20,7 +20,7 @@
 //
 // Software pipeline: two accumulator sets alternate between tiles. While the
 // products of tile t accumulate into one set, the running argmax of tile t-1
-// is taken from the other, a quarter of an accumulator per k-step, so that its
+// is taken from the other, half of one accumulator per k-step, so that its
 // vector instructions issue in the shadow of that k-step's matrix products
 // (each k-step is a scheduling region of its own; it also reads the next
 // k-step's A fragments from LDS).
