@@ -348,6 +348,12 @@ class Assign(Workload):
         return {"workload": self.x.name, "call": "idx_assign", "N": N, "C": self.x.c.shape[0],
                 "D": D, "inputs": "bf16", "accumulate": "f32 (MFMA)"}
 
+    def mfma_floor_shape(self):
+        """The assignment kernel's grid (256 points per workgroup) and its products
+        per wave (32 per tile of 64 centroids), as rounds of four."""
+        N, C = self.x.x.shape[0], self.x.c.shape[0]
+        return -(-N // 256), -(-C // 64) * 8
+
     def oracle_call(self, i):
         import oracle
         n, N = self.SAMPLE, self.x.x.shape[0]
@@ -710,10 +716,29 @@ def floors(torch, idx, wl, steps, flush):
         res[key + "_us"] = best[0]
         res[key + "_launch"] = f"{best[1]} x {best[2]}"
     res["read_GBps"] = nbytes / (res["read_us"] * 1e-6) / 1e9
+    if hasattr(wl, "mfma_floor_shape"):
+        # the same number of bf16 products as the call, on the same grid, with
+        # register operands: the matrix rate the chip sustains at its clock under
+        # load (the operand data sets the power draw and so the clock)
+        import numpy as np
+        from synth import f32_to_bf16_bits
+        blocks, iters = wl.mfma_floor_shape()
+        msink = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+        # operands like the call's: normal values in bf16 (the rate depends on the data)
+        frags = to_dev(f32_to_bf16_bits(np.random.default_rng(55).standard_normal(8192)
+                                        .astype(np.float32)))
+        g = capture(torch, lambda i: idx.idx_floor_mfma(frags, blocks, iters, msink), steps)
+        g.replay()
+        t = min(replay_ms(torch, g, steps) for _ in range(3))
+        del g
+        flops = 2 * 32 * 32 * 16 * 4 * iters * 4 * blocks
+        res["mfma_us"] = t * 1e3
+        res["mfma_launch"] = f"{blocks} x 256, {4 * iters} products per wave"
+        res["mfma_TFLOPs"] = flops / (t * 1e-3) / 1e12
     return res
 
 
-def roofline(wl, ms, traffic):
+def roofline(wl, ms, traffic, floor=None):
     if wl.w == 5:
         achieved = wl.alg_flops / (ms * 1e-3) / 1e12
         r = {"bound": "mfma", "kernel": KERNEL[wl.w], "achieved": achieved,
@@ -721,6 +746,10 @@ def roofline(wl, ms, traffic):
              "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
              "alg_flops_per_launch": wl.alg_flops, "alg_bytes_per_launch": wl.alg_bytes,
              "hbm_frac": wl.alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if floor and "mfma_TFLOPs" in floor:
+            # context, not the peak: back-to-back products on register operands
+            r["sustained_mfma_TFLOPs"] = floor["mfma_TFLOPs"]
+            r["frac_of_sustained"] = achieved / floor["mfma_TFLOPs"]
     else:
         achieved = wl.alg_bytes / (ms * 1e-3) / 1e9
         r = {"bound": "hbm", "kernel": KERNEL[wl.w], "achieved": achieved,
@@ -793,9 +822,12 @@ def measure(torch, idx, wl, steps, warmup, extras, flush):
         res["floor"] = floors(torch, idx, wl, steps, flush)
         log(f"[bench] w{wl.w} floors: read {res['floor']['read_us']:.2f} us, read + hand-off "
             f"{res['floor']['read_handoff_us']:.2f} us, empty {res['floor']['empty_us']:.2f} us")
+        if "mfma_us" in res["floor"]:
+            log(f"[bench] w{wl.w} floor: the call's products on register operands "
+                f"{res['floor']['mfma_us']:.1f} us, {res['floor']['mfma_TFLOPs']:.0f} TFLOP/s")
     else:
         del g
-    res["roofline"] = roofline(wl, ms, read_traffic(wl.w))
+    res["roofline"] = roofline(wl, ms, read_traffic(wl.w), res.get("floor"))
     return res, outs
 
 

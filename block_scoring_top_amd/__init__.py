@@ -16,7 +16,7 @@ import torch
 __all__ = ["idx_score", "idx_topk", "idx_topk_bf16", "idx_select", "idx_select_noalloc", "idx_select_paged", "idx_select_prefill",
            "idx_prefill_workspace_bytes", "idx_pool_keys", "idx_assign", "idx_workspace_bytes",
            "idx_topk_workspace_bytes", "idx_assign_workspace_bytes", "idx_status_string",
-           "idx_floor_empty", "idx_floor_read", "lib_path", "load", "IDX_SORTED", "IDX_RADIX8",
+           "idx_floor_empty", "idx_floor_read", "idx_floor_mfma", "lib_path", "load", "IDX_SORTED", "IDX_RADIX8",
            "IdxError",
            "SelectPlan", "plan_for"]
 
@@ -59,6 +59,7 @@ _SIGS = {
     "idx_plan_destroy": (None, [_vp]),
     "idx_floor_empty": (_c_int, [_c_int, _vp]),
     "idx_floor_read": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _vp]),
+    "idx_floor_mfma": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
 }
 
 _lib = None
@@ -385,6 +386,17 @@ def idx_floor_read(src, nbytes, sink, ticket=None, blocks=256, threads=256):
         raise ValueError("idx_floor_read: buffer too small")
     _check("idx_floor_read", load().idx_floor_read(_ptr(src), nbytes, _ptr(sink), _ptr(ticket),
                                                    blocks, threads, _stream(dev)))
+
+
+def idx_floor_mfma(frags, blocks, iters, sink):
+    """`blocks` x 4 waves of back-to-back bf16 matrix products, `iters` rounds of
+    four per wave on operands from `frags` (16 KiB; measurement floor); each
+    thread writes one word to `sink`."""
+    dev = _dev(frags, sink)
+    if frags.numel() * frags.element_size() < 16384 or sink.numel() < 256 * blocks:
+        raise ValueError("idx_floor_mfma: buffer too small")
+    _check("idx_floor_mfma", load().idx_floor_mfma(_ptr(frags), blocks, iters, _ptr(sink),
+                                                   _stream(dev)))
 
 
 class SelectPlan:

@@ -1,7 +1,8 @@
-// Floor launches for the benchmark: an empty kernel, and a plain streaming read
-// of a byte range, optionally followed by the arrival counter of the fused
-// select (relaxed agent-scope ticket after the workgroup's loads complete; the
-// last arriver returns it to zero). Nothing of the method is computed here.
+// Floor launches for the benchmark: an empty kernel, a plain streaming read of
+// a byte range, optionally followed by the arrival counter of the fused select
+// (relaxed agent-scope ticket after the workgroup's loads complete; the last
+// arriver returns it to zero), and back-to-back bf16 matrix products on
+// register operands. Nothing of the method is computed here.
 #include <hip/hip_runtime.h>
 
 #include "idx.h"
@@ -47,7 +48,49 @@ __global__ __launch_bounds__(NT) void floor_read_kernel(const uint4* __restrict_
   }
 }
 
+typedef __bf16 fbf16x8 __attribute__((ext_vector_type(8)));
+typedef float ff32x16 __attribute__((ext_vector_type(16)));
+
+// Four independent accumulator chains per wave, so that no product waits on
+// the one before it; the operands cycle through eight A and eight B fragments.
+__global__ __launch_bounds__(256, 2) void floor_mfma_kernel(const uint4* __restrict__ frags,
+                                                            int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  fbf16x8 a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = __builtin_bit_cast(fbf16x8, frags[k * 64 + lane]);
+    b[k] = __builtin_bit_cast(fbf16x8, frags[(8 + k) * 64 + lane]);
+  }
+  ff32x16 acc[4];
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+  for (int it = 0; it < iters; it += 8) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[(r + c) & 7], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace idxk
+
+extern "C" int idx_floor_mfma(const void* frags, int blocks, int iters, float* sink,
+                              void* stream) {
+  if (frags == nullptr || sink == nullptr || blocks < 1 || blocks > 65536 || iters < 8 ||
+      iters > 16384 || iters % 8 != 0 || reinterpret_cast<uintptr_t>(frags) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return IDX_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(idxk::floor_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(frags), iters,
+                     sink);
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_HIP;
+}
 
 extern "C" int idx_floor_empty(int blocks, void* stream) {
   if (blocks < 1 || blocks > 65536) return IDX_ERR_INVALID_ARG;

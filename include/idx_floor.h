@@ -8,8 +8,9 @@
  * the HBM bandwidth. These entry points measure that floor on the machine at
  * hand: an empty launch, and a plain streaming read of a byte range, optionally
  * followed by the same cross-workgroup arrival counter that the fused select
- * uses to hand a row to its last workgroup. They compute nothing of the method
- * and serve only as measurement context.
+ * uses to hand a row to its last workgroup; and a run of back-to-back matrix
+ * products, the rate the k-means assignment's products could reach at best.
+ * They compute nothing of the method and serve only as measurement context.
  *
  * Conventions are those of idx.h: device pointers owned by the caller, `stream`
  * is a hipStream_t passed as void*, validation on the host before any launch,
@@ -39,6 +40,19 @@ int idx_floor_empty(int blocks, void* stream);
  * blocks in [1, 65536]; bytes > 0. */
 int idx_floor_read(const void* src, size_t bytes, float* sink, uint32_t* ticket, int blocks,
                    int threads, void* stream);
+
+/* The matrix-core floor: `blocks` workgroups of 256 threads (four waves), each
+ * wave issuing `iters` rounds (a multiple of 8) of four independent
+ * v_mfma_f32_32x32x16_bf16 (2 * 32 * 32 * 16 * 4 * iters flops per wave) on
+ * register operands read once from `frags` (device, 16 KiB: eight A fragments
+ * then eight B fragments, each 64 lanes x 8 bf16, lane-major; round r uses A
+ * fragment r % 8 and, in chain c, B fragment (r + c) % 8). Every thread then
+ * writes the sum of its 64 accumulator words to `sink` (device, at least
+ * 256 * blocks floats; with all-ones fragments each word is 1024 * iters). It
+ * shows the bf16 matrix rate the chip sustains under load, which depends on
+ * the clock that load allows and so on the operand data: random fragments
+ * give the realistic figure. blocks in [1, 65536]; iters in [8, 16384]. */
+int idx_floor_mfma(const void* frags, int blocks, int iters, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

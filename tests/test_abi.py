@@ -308,6 +308,17 @@ def test_floor_launches_reject_bad_arguments(lib):
     assert r(P, 1024, P, None, 0, 256, None) == INVALID         # no workgroups
     assert r(P, 1024, P, None, 4, 512, None) == INVALID         # unsupported block size
     assert r(P, 1024, P, P + 2, 4, 256, None) == INVALID        # misaligned ticket
+    assert "idx_floor_mfma" in declared()
+    m = lib.idx_floor_mfma
+    assert m(None, 4, 8, P, None) == INVALID                    # no fragments
+    assert m(P, 4, 8, None, None) == INVALID                    # no sink
+    assert m(P, 0, 8, P, None) == INVALID                       # no workgroups
+    assert m(P, 65537, 8, P, None) == INVALID                   # too many
+    assert m(P, 4, 0, P, None) == INVALID                       # no products
+    assert m(P, 4, 12, P, None) == INVALID                      # not whole rounds of eight
+    assert m(P, 4, 16392, P, None) == INVALID                   # beyond the exact-sum range
+    assert m(P + 8, 4, 8, P, None) == INVALID                   # misaligned fragments
+    assert m(P, 4, 8, P + 2, None) == INVALID                   # misaligned sink
 
 
 def plan_create(lib, **kw):

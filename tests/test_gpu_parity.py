@@ -359,6 +359,19 @@ def test_workload_assign():
 
 
 @pytest.mark.gpu
+def test_floor_mfma_sums_in_closed_form():
+    """Each thread's 64 accumulator words after `iters` rounds of 32x32x16
+    products of all-ones operands hold 16 * iters each: 1024 * iters in all."""
+    import torch
+    frags = torch.full((8192,), 0x3F80, dtype=torch.int16, device="cuda")  # bf16 1.0
+    for blocks, iters in ((1, 8), (3, 40), (300, 128)):
+        sink = torch.full((256 * blocks,), -1.0, dtype=torch.float32, device="cuda")
+        idx.idx_floor_mfma(frags, blocks, iters, sink)
+        torch.cuda.synchronize()
+        assert (sink.cpu().numpy() == 1024.0 * iters).all(), (blocks, iters)
+
+
+@pytest.mark.gpu
 def test_floor_launches_run_and_leave_the_ticket_at_zero():
     import torch
     src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
