@@ -61,8 +61,8 @@ int launch_topk_bf16(const void* scores, const int32_t* n_valid, int32_t* ids, i
     const int cstride = (S * K + 3) / 4 * 4;
     char* w = static_cast<char*>(split_ws);
     uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
-    float* cs = reinterpret_cast<float*>(w + topk_ticket_bytes(B));
-    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_ticket_bytes(B) + (size_t)B * cstride * 4);
+    float* cs = reinterpret_cast<float*>(w + topk_cand_offset());
+    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_cand_offset() + (size_t)B * cstride * 4);
     const dim3 g2((unsigned)((int64_t)B * S));
     const bool merge2 = (int64_t)S * K <= kTopkNT * 2 * 4;
 #define IDX_LAUNCH_SPLIT16(SO, MS)                                                             \
@@ -111,7 +111,7 @@ size_t topk_split_workspace_bytes(int B, int N, int K) {
   const int S = topk_segments(B, N, K);
   if (S <= 1) return 0;
   const size_t cstride = ((size_t)S * K + 3) / 4 * 4;
-  return topk_ticket_bytes(B) + (size_t)B * cstride * 8;
+  return topk_cand_offset() + (size_t)B * cstride * 8;
 }
 
 int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,

@@ -19,6 +19,13 @@ constexpr int kTicketStride = 32;
 inline size_t topk_ticket_bytes(int B) {
   return ((size_t)B * kTicketStride * 4 + 255) / 256 * 256;
 }
+// Rows are cut into segments only when there are at most kTopkSplitMaxRows of
+// them (topk_segments). Their arrival counters take the workspace's first
+// topk_ticket_bytes(kTopkSplitMaxRows) bytes whatever the row count, and the
+// candidates follow: a later call with more rows then never finds an earlier
+// call's candidates where its own counters lie.
+constexpr int kTopkSplitMaxRows = 256;
+inline size_t topk_cand_offset() { return topk_ticket_bytes(kTopkSplitMaxRows); }
 constexpr int kTopkNT = 1024;   // top-K workgroup: 16 waves
 constexpr int kTopkSlots = 8;   // register tile: 1024*8*4 = 32768 keys
 
@@ -228,7 +235,7 @@ inline int topk_segments(int B, int N, int K) {
   // more workgroups while a row's segments stay long (at least 4096 entries and
   // twice K) and the candidates fit one register tile of the merge
   int S = 1;
-  while (S < 8 && (int64_t)B * S * 2 <= 512 && N / (S * 2) >= 4096 && N / (S * 2) >= 2 * K &&
+  while (S < 8 && B <= kTopkSplitMaxRows && (int64_t)B * S * 2 <= 512 && N / (S * 2) >= 4096 && N / (S * 2) >= 2 * K &&
          (int64_t)(S * 2) * K <= kTopkNT * kTopkSlots * 4)
     S *= 2;
   return S;
@@ -247,8 +254,8 @@ int launch_topk_f32(const void* scores, const int32_t* n_valid, int32_t* ids, in
     const int cstride = (S * K + 3) / 4 * 4;
     char* w = static_cast<char*>(split_ws);
     uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
-    float* cs = reinterpret_cast<float*>(w + topk_ticket_bytes(B));
-    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_ticket_bytes(B) + (size_t)B * cstride * 4);
+    float* cs = reinterpret_cast<float*>(w + topk_cand_offset());
+    int32_t* ci = reinterpret_cast<int32_t*>(w + topk_cand_offset() + (size_t)B * cstride * 4);
     const dim3 g2((unsigned)((int64_t)B * S));
     const bool merge2 = (int64_t)S * K <= kTopkNT * 2 * 4;
 #define IDX_LAUNCH_SPLIT(SO, MS)                                                            \

@@ -71,9 +71,12 @@ def test_workspace_sizes(lib):
 
 
 def test_topk_workspace_sizes(lib):
-    # few long rows: arrival lines (256-byte aligned) + B * round_up(S*K, 4) candidate
-    # scores and ids; here S = 4 segments (64 rows x 30000, K = 2048)
-    assert lib.idx_topk_workspace_bytes(64, 30000, 2048, 0) == 64 * 128 + 64 * 8192 * 8
+    # few long rows: arrival lines for the most rows that are ever split (256 of
+    # 128 bytes, whatever B is) + B * round_up(S*K, 4) candidate scores and ids;
+    # here S = 4 segments (64 rows x 30000, K = 2048)
+    assert lib.idx_topk_workspace_bytes(64, 30000, 2048, 0) == 256 * 128 + 64 * 8192 * 8
+    assert lib.idx_topk_workspace_bytes(3, 40000, 100, 0) == 256 * 128 + 3 * 800 * 8
+    assert lib.idx_topk_workspace_bytes(257, 40000, 100, 0) == 0   # no row is split
     assert lib.idx_topk_workspace_bytes(1000, 30000, 10, 0) == 0   # enough rows already
     assert lib.idx_topk_workspace_bytes(64, 2000, 10, 0) == 0       # short rows
     assert lib.idx_topk_workspace_bytes(0, 30000, 10, 0) == 0

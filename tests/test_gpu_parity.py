@@ -277,6 +277,26 @@ def test_topk_long_rows_split_into_segments(K, sorted_out):
     np.testing.assert_array_equal(counts2, counts)
 
 
+def test_topk_workspace_serves_later_calls_with_other_row_counts():
+    """One workspace for split calls whose row counts grow and shrink: an earlier
+    call's segment candidates must not lie where a later call's arrival counters
+    are (a counter left nonzero leaves its row unmerged and its outputs
+    unwritten). Outputs poisoned with 0xa5 bytes before every call."""
+    shapes = [(9, 20675, 37), (20, 22957, 2), (5, 30000, 2048), (64, 30000, 2048),
+              (3, 40000, 100), (40, 20000, 700), (9, 20675, 37)]
+    nbytes = max(idx.idx_topk_workspace_bytes(B, N, K) for B, N, K in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for i, (B, N, K) in enumerate(shapes):
+        assert idx.idx_topk_workspace_bytes(B, N, K) > 0  # the split path
+        x = synth.make_topk(B, N, K, 430 + i)
+        say(f"[topk] shared workspace, call {i}: B={B} N={N} K={K}")
+        ids = torch.full((B, K), -1515870811, dtype=torch.int32, device="cuda")
+        counts = torch.full((B,), -1515870811, dtype=torch.int32, device="cuda")
+        idx.idx_topk(to_dev(x.scores), K, None, i % 2 == 1, ids=ids, counts=counts, ws=ws)
+        torch.cuda.synchronize()
+        check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), x.scores, None, K, i % 2 == 1)
+
+
 @pytest.mark.parametrize("N", [1, 3, 1000, 8191, 8192, 32768, 32769, 70001])
 def test_topk_lengths(N):
     """Row lengths around the layouts: one 2-slot tile (up to 8191 entries a

@@ -1,0 +1,138 @@
+"""Seeded random call shapes against the oracle. Each case draws its shape from a
+fixed seed (so a failure names a reproducible case): idx_select over both input
+types, score order or index order, the 8-bit radix variant, head counts up to
+64, row lengths from one block to 20000, K from 1 to 4096, request lengths at
+and around the block and row boundaries; idx_topk and idx_topk_bf16 over the
+nine stress distributions with and without per-row valid counts. Outputs are
+poisoned with 0xa5 bytes first; ids, their order, the -1 padding and the
+counts are compared word for word with the oracle's selection from the GPU's
+own scores, and the scores against fp64 within the tolerance of their type
+("Round 18 Track C", section 2: bitwise parity over many shapes, poisoned
+unused slots)."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+from tests.helpers import RTOL, check_ids_band, check_ids_exact, check_scores, to_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scoring_top_amd as idx  # noqa: E402
+
+POISON = -1515870811  # 0xa5a5a5a5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def draw_select(seed):
+    rng = np.random.default_rng(7000 + seed)
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    B = int(rng.integers(1, 10))
+    H = int(rng.choice([1, 2, 3, 4, 7, 16, 64]))
+    N_pad = int([rng.integers(1, 300), rng.integers(300, 3000),
+                 rng.integers(3000, 20001)][int(rng.integers(3))])
+    while B * N_pad * H > 3_000_000 and N_pad > 1:  # keep the fp64 oracle quick
+        N_pad //= 2
+    K = int([1, 2, rng.integers(1, 65), rng.integers(65, 600),
+             rng.integers(600, 4097)][int(rng.integers(5))])
+    srt = bool(rng.integers(2))
+    radix8 = bool(rng.random() < 0.3)
+    top = N_pad * 16
+    picks = [0, 1, 15, 16, 17, top - 1, top, top + 5, 16 * min(K, N_pad), 16 * min(K, N_pad) + 1]
+    seq = [int(picks[int(rng.integers(len(picks)))]) if rng.random() < 0.5
+           else int(rng.integers(0, top + 1)) for _ in range(B)]
+    seq = [max(0, s) for s in seq]
+    return dict(dtype=dtype, B=B, H=H, N_pad=N_pad, K=K, srt=srt, radix8=radix8, seq=seq)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_select_shapes(seed):
+    p = draw_select(seed)
+    say(f"[random select {seed}] {p}")
+    x = synth.make_indexer(p["B"], p["H"], 128, p["N_pad"], p["seq"], p["K"], p["dtype"],
+                           7100 + seed, sorted_out=p["srt"])
+    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+    B, K = p["B"], p["K"]
+    ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    counts = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select(q, c, sl, K, sorted=p["srt"], ids=ids, counts=counts,
+                             return_scores=True, radix8=p["radix8"])
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+    nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+    check_scores(s, S, A, RTOL[x.dtype])
+    ids_np, counts_np = ids.cpu().numpy(), counts.cpu().numpy()
+    check_ids_exact(ids_np, counts_np, s, nv, K, p["srt"])
+    check_ids_band(ids_np, S, A, nv, K, RTOL[x.dtype])
+    # the form without a score output (staged scores) returns the same words
+    ids2 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    counts2 = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    idx.idx_select(q, c, sl, K, sorted=p["srt"], ids=ids2, counts=counts2, radix8=p["radix8"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
+    np.testing.assert_array_equal(counts2.cpu().numpy(), counts_np)
+
+
+def draw_topk(seed):
+    rng = np.random.default_rng(8000 + seed)
+    B = int(rng.integers(1, 71))
+    N = int([rng.integers(1, 2049), rng.integers(2049, 8193),
+             rng.integers(8193, 40001)][int(rng.integers(3))])
+    while B * N > 600_000 and B > 1:
+        B //= 2
+    K = int([1, 2, rng.integers(1, 65), rng.integers(65, 1025),
+             rng.integers(1025, 4097)][int(rng.integers(5))])
+    srt = bool(rng.integers(2))
+    with_nv = bool(rng.integers(2))
+    nv = None
+    if with_nv:
+        picks = [0, 1, K - 1, K, K + 1, N - 1, N]
+        nv = np.array([picks[int(rng.integers(len(picks)))] if rng.random() < 0.5
+                       else int(rng.integers(0, N + 1)) for _ in range(B)], np.int32)
+        nv = np.clip(nv, 0, N).astype(np.int32)
+    return dict(B=B, N=N, K=K, srt=srt, nv=nv, radix8=bool(rng.random() < 0.3))
+
+
+def run_topk(scores_h, scores_d, p, bf16):
+    B, K = p["B"], p["K"]
+    ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    counts = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    nvd = None if p["nv"] is None else torch.from_numpy(p["nv"]).to("cuda")
+    if bf16:
+        idx.idx_topk_bf16(scores_d, K, nvd, p["srt"], ids=ids, counts=counts)
+    else:
+        idx.idx_topk(scores_d, K, nvd, p["srt"], ids=ids, counts=counts, radix8=p["radix8"])
+    torch.cuda.synchronize()
+    check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), scores_h, p["nv"], K, p["srt"])
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_topk_shapes(seed):
+    p = draw_topk(seed)
+    say(f"[random topk {seed}] B={p['B']} N={p['N']} K={p['K']} sorted={p['srt']} "
+        f"valid counts={p['nv'] is not None} radix8={p['radix8']}")
+    x = synth.make_topk(p["B"], p["N"], p["K"], 8100 + seed)
+    run_topk(x.scores, to_dev(x.scores), p, False)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_topk_bf16_shapes(seed):
+    p = draw_topk(100 + seed)
+    say(f"[random topk bf16 {seed}] B={p['B']} N={p['N']} K={p['K']} sorted={p['srt']} "
+        f"valid counts={p['nv'] is not None}")
+    x = synth.make_topk(p["B"], p["N"], p["K"], 8200 + seed)
+    bits = synth.f32_to_bf16_bits(x.scores)
+    # the oracle selects from the same bf16 values, widened exactly
+    run_topk(synth.bf16_bits_to_f32(bits), to_dev(bits), p, True)
