@@ -2,13 +2,16 @@
 fixed seed (so a failure names a reproducible case): idx_select over both input
 types, score order or index order, the 8-bit radix variant, head counts up to
 64, row lengths from one block to 20000, K from 1 to 4096, request lengths at
-and around the block and row boundaries; idx_topk and idx_topk_bf16 over the
-nine stress distributions with and without per-row valid counts. Outputs are
-poisoned with 0xa5 bytes first; ids, their order, the -1 padding and the
-counts are compared word for word with the oracle's selection from the GPU's
-own scores, and the scores against fp64 within the tolerance of their type
-("Round 18 Track C", section 2: bitwise parity over many shapes, poisoned
-unused slots)."""
+and around the block and row boundaries, also through a resolved plan and
+through idx_select_noalloc; idx_topk and idx_topk_bf16 over the nine stress
+distributions with and without per-row valid counts; idx_select_paged with
+empty, clamped and invalid page lists; idx_select_prefill with ragged token
+and block tiles; idx_assign; idx_pool_keys. Outputs are poisoned with 0xa5
+bytes first; ids, their order, the -1 padding and the counts are compared word
+for word with the oracle's selection from the GPU's own scores, and the scores
+against fp64 within the tolerance of their type ("Round 18 Track C", section
+2: bitwise parity over many shapes, poisoned unused slots). All calls of one
+entry point share the binding's workspace, as a caller's calls would."""
 import sys
 
 import numpy as np
@@ -56,7 +59,7 @@ def draw_select(seed):
     return dict(dtype=dtype, B=B, H=H, N_pad=N_pad, K=K, srt=srt, radix8=radix8, seq=seq)
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_select_shapes(seed):
     p = draw_select(seed)
     say(f"[random select {seed}] {p}")
@@ -83,6 +86,21 @@ def test_random_select_shapes(seed):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
     np.testing.assert_array_equal(counts2.cpu().numpy(), counts_np)
+    if seed % 2 == 0 and not p["radix8"]:  # a resolved plan returns the same words
+        dt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+        plan = idx.plan_for(B, p["H"], p["N_pad"], K, dt, sorted=p["srt"])
+        ids3, counts3, _ = plan(q, c, sl)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids3.cpu().numpy(), ids_np)
+        np.testing.assert_array_equal(counts3.cpu().numpy(), counts_np)
+    if seed % 2 == 1 and B * ((p["N_pad"] + 3) // 4 * 4) * 4 <= (16 << 20) - 4096 * 128:
+        ids4 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+        counts4 = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+        idx.idx_select_noalloc(q, c, sl, K, sorted=p["srt"], ids=ids4, counts=counts4,
+                               radix8=p["radix8"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids4.cpu().numpy(), ids_np)
+        np.testing.assert_array_equal(counts4.cpu().numpy(), counts_np)
 
 
 def draw_topk(seed):
@@ -118,7 +136,7 @@ def run_topk(scores_h, scores_d, p, bf16):
     check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), scores_h, p["nv"], K, p["srt"])
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_topk_shapes(seed):
     p = draw_topk(seed)
     say(f"[random topk {seed}] B={p['B']} N={p['N']} K={p['K']} sorted={p['srt']} "
@@ -127,12 +145,123 @@ def test_random_topk_shapes(seed):
     run_topk(x.scores, to_dev(x.scores), p, False)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_topk_bf16_shapes(seed):
-    p = draw_topk(100 + seed)
+    p = draw_topk(1000 + seed)
     say(f"[random topk bf16 {seed}] B={p['B']} N={p['N']} K={p['K']} sorted={p['srt']} "
         f"valid counts={p['nv'] is not None}")
     x = synth.make_topk(p["B"], p["N"], p["K"], 8200 + seed)
     bits = synth.f32_to_bf16_bits(x.scores)
     # the oracle selects from the same bf16 values, widened exactly
     run_topk(synth.bf16_bits_to_f32(bits), to_dev(bits), p, True)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_paged_shapes(seed):
+    rng = np.random.default_rng(9000 + seed)
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    B = int(rng.integers(1, 41))
+    H = int(rng.choice([1, 4, 16]))
+    n_rows = int([rng.integers(1, 64), rng.integers(64, 20001)][int(rng.integers(2))])
+    hi = min(n_rows, 6000)
+    counts = [int([0, 1, hi, rng.integers(0, hi + 1)][int(rng.integers(4))]) for _ in range(B)]
+    while sum(counts) * H > 1_500_000:
+        counts = [n // 2 for n in counts]
+    K = int([1, 2, rng.integers(1, 300), rng.integers(300, 4097)][int(rng.integers(4))])
+    srt = bool(rng.integers(2))
+    mx = max(max(counts), 1)
+    max_pages = int([mx, max(1, mx // 2), mx + 37][int(rng.integers(3))])
+    x = synth.make_paged(B, H, 128, n_rows, counts, K, dtype, 9100 + seed, sorted_out=srt,
+                         max_pages=max_pages)
+    indices = x.indices.copy()
+    if indices.size and rng.random() < 0.5:  # entries that name no page
+        bad = rng.choice(indices.size, min(indices.size, 5), replace=False)
+        indices[bad] = np.where(rng.random(bad.size) < 0.5, -1, n_rows + 3)
+    say(f"[random paged {seed}] {dtype} B={B} H={H} pool={n_rows} pages={counts[:6]} "
+        f"max_pages={max_pages} K={K} sorted={srt}")
+    qd, cd = to_dev(x.q), to_dev(x.c_pool)
+    ipd, ixd = to_dev(x.indptr), to_dev(indices)
+    ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select_paged(qd, cd, ipd, ixd, K, max_pages, sorted=srt, ids=ids,
+                                   counts=cnt, return_scores=True)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    S, A, n_slots = oracle.score_paged(x.q, x.c_pool, x.indptr, indices, max_pages, dtype)
+    check_scores(s, S, A, RTOL[dtype])
+    ids_np, cnt_np = ids.cpu().numpy(), cnt.cpu().numpy()
+    check_ids_exact(ids_np, cnt_np, s, n_slots, K, srt)
+    check_ids_band(ids_np, S, A, n_slots, K, RTOL[dtype])
+    ids2 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    idx.idx_select_paged(qd, cd, ipd, ixd, K, max_pages, sorted=srt, ids=ids2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_prefill_shapes(seed):
+    rng = np.random.default_rng(9500 + seed)
+    B = int(rng.integers(1, 4))
+    T = int([1, rng.integers(1, 33), rng.integers(33, 160)][int(rng.integers(3))])
+    H = int(rng.choice([1, 3, 4, 16]))
+    N_pad = int([rng.integers(1, 64), rng.integers(64, 2600)][int(rng.integers(2))])
+    while B * T * N_pad * H > 6_000_000 and N_pad > 1:
+        N_pad //= 2
+    pos0 = [int([-7, 0, rng.integers(0, 16 * N_pad + 1), 16 * N_pad][int(rng.integers(4))])
+            for _ in range(B)]
+    K = int([1, rng.integers(1, 300), rng.integers(300, 1500)][int(rng.integers(3))])
+    srt = bool(rng.integers(2))
+    say(f"[random prefill {seed}] B={B} T={T} H={H} N_pad={N_pad} pos0={pos0} K={K} "
+        f"sorted={srt}")
+    x = synth.make_prefill(B, T, H, 128, N_pad, pos0, K, 9600 + seed, sorted_out=srt)
+    qd, cd, pd = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
+    ids = torch.full((B, T, K), POISON, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, T), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select_prefill(qd, cd, pd, K, sorted=srt, ids=ids, counts=cnt,
+                                     return_scores=True)
+    torch.cuda.synchronize()
+    R = B * T
+    s = s.cpu().numpy().reshape(R, -1)
+    S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+    S, A, NV = S.reshape(R, -1), A.reshape(R, -1), NV.reshape(R)
+    check_scores(s, S, A, RTOL[x.dtype])
+    ids_np, cnt_np = ids.cpu().numpy().reshape(R, K), cnt.cpu().numpy().reshape(R)
+    check_ids_exact(ids_np, cnt_np, s, NV, K, srt)
+    check_ids_band(ids_np, S, A, NV, K, RTOL[x.dtype])
+    ids2 = torch.full((B, T, K), POISON, dtype=torch.int32, device="cuda")
+    idx.idx_select_prefill(qd, cd, pd, K, sorted=srt, ids=ids2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy().reshape(R, K), ids_np)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_assign_shapes(seed):
+    from tests.helpers import check_assign
+    rng = np.random.default_rng(9800 + seed)
+    N = int([1, rng.integers(1, 300), rng.integers(300, 6000)][int(rng.integers(3))])
+    C = int([1, rng.integers(1, 64), rng.integers(64, 1600)][int(rng.integers(3))])
+    say(f"[random assign {seed}] N={N} C={C}")
+    x = synth.make_assign(N, C, 128, 9900 + seed)
+    a = torch.full((N,), POISON, dtype=torch.int32, device="cuda")
+    best = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    idx.idx_assign(to_dev(x.x), to_dev(x.c), assign=a, best=best, return_best=True)
+    torch.cuda.synchronize()
+    a_np, b_np = a.cpu().numpy(), best.cpu().numpy()
+    check_assign(a_np, b_np, x.x, x.c)
+    np.testing.assert_array_equal(a_np, x.comp)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_pool_shapes(seed):
+    from tests.test_gpu_pool import pool_check
+    rng = np.random.default_rng(9950 + seed)
+    B = int(rng.integers(1, 6))
+    page = int(rng.choice([1, 3, 16, 64]))
+    N_pad = int(rng.integers(1, 400))
+    S_pad = int(rng.integers(1, N_pad * page + 40))
+    seq = [int([0, 1, S_pad, rng.integers(0, S_pad + 1), S_pad + 9][int(rng.integers(5))])
+           for _ in range(B)]
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    say(f"[random pool {seed}] B={B} S_pad={S_pad} N_pad={N_pad} page={page} seq={seq} {dtype}")
+    pool_check(synth.make_keys(B, S_pad, 128, N_pad, seq, dtype, 9960 + seed, page_size=page,
+                               name=f"random_{seed}"))
