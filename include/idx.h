@@ -36,8 +36,12 @@
  *     matching *_workspace_bytes() returns. A workspace must be zero-filled
  *     once before its first use: it holds arrival counters, which every call
  *     returns to zero, and scratch, which calls overwrite before reading. One
- *     workspace may serve any sequence of calls on one stream; calls that may
- *     overlap (other streams) need distinct workspaces.
+ *     workspace may serve any sequence of calls on one stream whose sizes come
+ *     from the same *_workspace_bytes() function (idx_select, idx_select_paged
+ *     and plans share one layout, idx_topk and idx_topk_bf16 another; the
+ *     layouts differ, so a buffer used under one must be zero-filled again
+ *     before it serves another). Calls that may overlap (other streams) need
+ *     distinct workspaces.
  */
 #ifndef IDX_H
 #define IDX_H
