@@ -51,12 +51,16 @@ def draw_select(seed):
              rng.integers(600, 4097)][int(rng.integers(5))])
     srt = bool(rng.integers(2))
     radix8 = bool(rng.random() < 0.3)
-    top = N_pad * 16
-    picks = [0, 1, 15, 16, 17, top - 1, top, top + 5, 16 * min(K, N_pad), 16 * min(K, N_pad) + 1]
+    page = int([16, 16, 1, 7, 64][int(rng.integers(5))])
+    top = N_pad * page
+    picks = [0, 1, page - 1, page, page + 1, top - 1, top, top + 5, page * min(K, N_pad),
+             page * min(K, N_pad) + 1]
     seq = [int(picks[int(rng.integers(len(picks)))]) if rng.random() < 0.5
            else int(rng.integers(0, top + 1)) for _ in range(B)]
     seq = [max(0, s) for s in seq]
-    return dict(dtype=dtype, B=B, H=H, N_pad=N_pad, K=K, srt=srt, radix8=radix8, seq=seq)
+    chunk_log2 = int([0, 0, rng.integers(4, 15)][int(rng.integers(3))])
+    return dict(dtype=dtype, B=B, H=H, N_pad=N_pad, K=K, srt=srt, radix8=radix8, seq=seq,
+                page=page, chunk_log2=chunk_log2)
 
 
 @pytest.mark.parametrize("seed", range(96))
@@ -64,12 +68,12 @@ def test_random_select_shapes(seed):
     p = draw_select(seed)
     say(f"[random select {seed}] {p}")
     x = synth.make_indexer(p["B"], p["H"], 128, p["N_pad"], p["seq"], p["K"], p["dtype"],
-                           7100 + seed, sorted_out=p["srt"])
+                           7100 + seed, sorted_out=p["srt"], page_size=p["page"])
     q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
-    B, K = p["B"], p["K"]
+    B, K, pg = p["B"], p["K"], p["page"]
     ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
     counts = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
-    _, _, s = idx.idx_select(q, c, sl, K, sorted=p["srt"], ids=ids, counts=counts,
+    _, _, s = idx.idx_select(q, c, sl, K, page_size=pg, sorted=p["srt"], ids=ids, counts=counts,
                              return_scores=True, radix8=p["radix8"])
     torch.cuda.synchronize()
     s = s.cpu().numpy()
@@ -79,16 +83,19 @@ def test_random_select_shapes(seed):
     ids_np, counts_np = ids.cpu().numpy(), counts.cpu().numpy()
     check_ids_exact(ids_np, counts_np, s, nv, K, p["srt"])
     check_ids_band(ids_np, S, A, nv, K, RTOL[x.dtype])
-    # the form without a score output (staged scores) returns the same words
+    # the standalone scoring kernel on the same inputs
+    check_scores(idx.idx_score(q, c, sl, page_size=pg).cpu().numpy(), S, A, RTOL[x.dtype])
+    # the form without a score output (staged scores, any chunking) returns the same words
     ids2 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
     counts2 = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
-    idx.idx_select(q, c, sl, K, sorted=p["srt"], ids=ids2, counts=counts2, radix8=p["radix8"])
+    idx.idx_select(q, c, sl, K, page_size=pg, sorted=p["srt"], ids=ids2, counts=counts2,
+                   radix8=p["radix8"], chunk_log2=p["chunk_log2"])
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
     np.testing.assert_array_equal(counts2.cpu().numpy(), counts_np)
     if seed % 2 == 0 and not p["radix8"]:  # a resolved plan returns the same words
         dt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
-        plan = idx.plan_for(B, p["H"], p["N_pad"], K, dt, sorted=p["srt"])
+        plan = idx.plan_for(B, p["H"], p["N_pad"], K, dt, page_size=pg, sorted=p["srt"])
         ids3, counts3, _ = plan(q, c, sl)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(ids3.cpu().numpy(), ids_np)
@@ -96,8 +103,8 @@ def test_random_select_shapes(seed):
     if seed % 2 == 1 and B * ((p["N_pad"] + 3) // 4 * 4) * 4 <= (16 << 20) - 4096 * 128:
         ids4 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
         counts4 = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
-        idx.idx_select_noalloc(q, c, sl, K, sorted=p["srt"], ids=ids4, counts=counts4,
-                               radix8=p["radix8"])
+        idx.idx_select_noalloc(q, c, sl, K, page_size=pg, sorted=p["srt"], ids=ids4,
+                               counts=counts4, radix8=p["radix8"])
         torch.cuda.synchronize()
         np.testing.assert_array_equal(ids4.cpu().numpy(), ids_np)
         np.testing.assert_array_equal(counts4.cpu().numpy(), counts_np)
