@@ -272,3 +272,70 @@ def test_random_pool_shapes(seed):
     say(f"[random pool {seed}] B={B} S_pad={S_pad} N_pad={N_pad} page={page} seq={seq} {dtype}")
     pool_check(synth.make_keys(B, S_pad, 128, N_pad, seq, dtype, 9960 + seed, page_size=page,
                                name=f"random_{seed}"))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_graph_replays(seed):
+    """Random select and top-K shapes captured into one HIP graph (two calls of
+    each, workspaces passed in), replayed three times with the outputs poisoned
+    before each replay and eager calls of other shapes on the same workspaces
+    between replays: every replay's ids and counts equal the oracle's."""
+    p = draw_select(500 + seed)
+    t = draw_topk(500 + seed)
+    say(f"[random graph {seed}] select {p} topk B={t['B']} N={t['N']} K={t['K']}")
+    x = synth.make_indexer(p["B"], p["H"], 128, p["N_pad"], p["seq"], p["K"], p["dtype"],
+                           7300 + seed, sorted_out=p["srt"], page_size=p["page"])
+    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+    B, K, pg = p["B"], p["K"], p["page"]
+    y = synth.make_topk(t["B"], t["N"], t["K"], 8300 + seed)
+    sc = to_dev(y.scores)
+    nvd = None if t["nv"] is None else torch.from_numpy(t["nv"]).to("cuda")
+    ws_s = torch.zeros(idx.idx_workspace_bytes(B, p["N_pad"], p["H"], K), dtype=torch.uint8,
+                       device="cuda")
+    ws_t = torch.zeros(max(256, idx.idx_topk_workspace_bytes(t["B"], t["N"], t["K"])),
+                       dtype=torch.uint8, device="cuda")
+    # the GPU's scores of this select, checked against fp64, fix the expected ids
+    _, _, s = idx.idx_select(q, c, sl, K, page_size=pg, sorted=p["srt"], return_scores=True,
+                             ws=ws_s)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+    check_scores(s, S, A, RTOL[x.dtype])
+    nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+    ids = torch.empty(B, K, dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    tids = torch.empty(t["B"], t["K"], dtype=torch.int32, device="cuda")
+    tcounts = torch.empty(t["B"], dtype=torch.int32, device="cuda")
+
+    def calls():
+        idx.idx_select(q, c, sl, K, page_size=pg, sorted=p["srt"], ids=ids, counts=counts,
+                       ws=ws_s)
+        idx.idx_topk(sc, t["K"], nvd, t["srt"], ids=tids, counts=tcounts, ws=ws_t)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+        calls()
+    other = draw_select(600 + seed)
+    xo = synth.make_indexer(min(other["B"], B), p["H"], 128, p["N_pad"],
+                            other["seq"][:min(other["B"], B)], K, p["dtype"], 7400 + seed,
+                            page_size=pg)
+    for rep in range(3):
+        for o in (ids, counts, tids, tcounts):
+            o.fill_(POISON)
+        g.replay()
+        torch.cuda.synchronize()
+        check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, p["srt"])
+        check_ids_exact(tids.cpu().numpy(), tcounts.cpu().numpy(), y.scores, t["nv"], t["K"],
+                        t["srt"])
+        # eager work of another shape on the same workspaces between the replays
+        idx.idx_select(to_dev(xo.q), to_dev(xo.c), to_dev(xo.seq_len), K, page_size=pg,
+                       ws=ws_s)
+        idx.idx_topk(sc[: max(1, t["B"] // 2)], t["K"], None, not t["srt"], ws=ws_t)
+        torch.cuda.synchronize()
