@@ -339,3 +339,38 @@ def test_random_graph_replays(seed):
                        ws=ws_s)
         idx.idx_topk(sc[: max(1, t["B"] // 2)], t["K"], None, not t["srt"], ws=ws_t)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_long_select_rows(seed):
+    """Requests longer than a 1024-thread workgroup's register tile (32768
+    entries): the selecting workgroup streams the staged row through its tile."""
+    rng = np.random.default_rng(7700 + seed)
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    B = int(rng.integers(1, 4))
+    H = int(rng.choice([1, 4]))
+    N_pad = int(rng.integers(32769, 80001))
+    K = int([1, rng.integers(2, 300), rng.integers(300, 4097)][int(rng.integers(3))])
+    srt = bool(rng.integers(2))
+    top = N_pad * 16
+    seq = [int([top, top - 1, rng.integers(0, top + 1), 16 * 32768 + 16][int(rng.integers(4))])
+           for _ in range(B)]
+    say(f"[random long rows {seed}] {dtype} B={B} H={H} N_pad={N_pad} K={K} sorted={srt} "
+        f"seq={seq}")
+    x = synth.make_indexer(B, H, 128, N_pad, seq, K, dtype, 7800 + seed, sorted_out=srt)
+    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+    ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    counts = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select(q, c, sl, K, sorted=srt, ids=ids, counts=counts, return_scores=True)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+    nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+    check_scores(s, S, A, RTOL[x.dtype])
+    ids_np, counts_np = ids.cpu().numpy(), counts.cpu().numpy()
+    check_ids_exact(ids_np, counts_np, s, nv, K, srt)
+    check_ids_band(ids_np, S, A, nv, K, RTOL[x.dtype])
+    ids2 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    idx.idx_select(q, c, sl, K, sorted=srt, ids=ids2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
