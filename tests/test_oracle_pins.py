@@ -352,6 +352,23 @@ def test_select_matches_rank_definition_exhaustively(L):
                     assert list(got) == _rank_select(s, nv, K, srt), (row, nv, K, srt)
 
 
+def test_select_matches_rank_definition_on_random_rows():
+    """Longer rows than the exhaustive case, drawn from a fixed seed: tied
+    values, signed zeros and -inf, valid counts inside the row, K around the
+    number of candidates, both output orders."""
+    rng = np.random.default_rng(3131)
+    pool = np.array([-np.inf, -2.5, -1.0, -0.0, 0.0, 0.5, 1.0, 1.5, 3.0], dtype=np.float32)
+    for _ in range(300):
+        L = int(rng.integers(0, 61))
+        s = pool[rng.integers(0, pool.size, L)] if rng.random() < 0.7 else \
+            rng.standard_normal(L).astype(np.float32)
+        nv = int(rng.integers(0, L + 1))
+        K = int(rng.integers(1, L + 3))
+        srt = bool(rng.integers(2))
+        assert list(oracle.select_row(s, nv, K, srt)) == _rank_select(s, nv, K, srt), (
+            list(s), nv, K, srt)
+
+
 def test_select_rank_definition_on_each_stress_distribution():
     """O(N^2) rank counting (vectorised) on one row of each distribution."""
     x = synth.make_topk(9, 2500, 300, 31)
