@@ -376,3 +376,42 @@ def test_random_long_select_rows(seed):
     idx.idx_select(q, c, sl, K, sorted=srt, ids=ids2)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_select_many_requests(seed):
+    """More than 32 requests: the 512-thread instances (one or four key slots,
+    blocked or striped rows), and score-ordered K above 1024 back on the
+    1024-thread ones."""
+    rng = np.random.default_rng(7900 + seed)
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    B = int(rng.integers(33, 301))
+    H = int(rng.choice([1, 4, 16]))
+    N_pad = int([rng.integers(1, 600), rng.integers(600, 2049), rng.integers(2049, 9000)][
+        int(rng.integers(3))])
+    while B * N_pad * H > 3_000_000 and N_pad > 1:
+        N_pad //= 2
+    K = int([1, rng.integers(2, 257), rng.integers(257, 1025), rng.integers(1025, 2049)][
+        int(rng.integers(4))])
+    srt = bool(rng.integers(2))
+    top = N_pad * 16
+    seq = [int([0, top, rng.integers(0, top + 1), 16 * min(K, N_pad)][int(rng.integers(4))])
+           for _ in range(B)]
+    say(f"[random many requests {seed}] {dtype} B={B} H={H} N_pad={N_pad} K={K} sorted={srt}")
+    x = synth.make_indexer(B, H, 128, N_pad, seq, K, dtype, 7950 + seed, sorted_out=srt)
+    q, c, sl = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len)
+    ids = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    counts = torch.full((B,), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select(q, c, sl, K, sorted=srt, ids=ids, counts=counts, return_scores=True)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+    nv = oracle.n_valid(x.seq_len, x.page_size, x.N_pad)
+    check_scores(s, S, A, RTOL[x.dtype])
+    ids_np, counts_np = ids.cpu().numpy(), counts.cpu().numpy()
+    check_ids_exact(ids_np, counts_np, s, nv, K, srt)
+    check_ids_band(ids_np, S, A, nv, K, RTOL[x.dtype])
+    ids2 = torch.full((B, K), POISON, dtype=torch.int32, device="cuda")
+    idx.idx_select(q, c, sl, K, sorted=srt, ids=ids2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
