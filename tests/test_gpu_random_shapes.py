@@ -415,3 +415,27 @@ def test_random_select_many_requests(seed):
     idx.idx_select(q, c, sl, K, sorted=srt, ids=ids2)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids2.cpu().numpy(), ids_np)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_topk_many_short_rows(seed):
+    """At least 512 rows of at most 2048 entries: the 256-thread instances (K up
+    to 1024), fp32 and bf16 rows, with and without valid counts."""
+    rng = np.random.default_rng(8600 + seed)
+    B = int(rng.integers(512, 3001))
+    N = int([rng.integers(1, 200), rng.integers(200, 2049)][int(rng.integers(2))])
+    K = int([1, rng.integers(2, 65), rng.integers(65, 1025)][int(rng.integers(3))])
+    srt = bool(rng.integers(2))
+    nv = None
+    if rng.integers(2):
+        nv = np.clip(rng.integers(-3, N + 5, B), -3, N + 5).astype(np.int32)
+    bf16 = bool(rng.integers(2))
+    p = dict(B=B, N=N, K=K, srt=srt, nv=nv, radix8=not bf16 and bool(rng.random() < 0.3))
+    say(f"[random many short rows {seed}] B={B} N={N} K={K} sorted={srt} "
+        f"valid counts={nv is not None} bf16={bf16} radix8={p['radix8']}")
+    x = synth.make_topk(B, N, K, 8700 + seed)
+    if bf16:
+        bits = synth.f32_to_bf16_bits(x.scores)
+        run_topk(synth.bf16_bits_to_f32(bits), to_dev(bits), p, True)
+    else:
+        run_topk(x.scores, to_dev(x.scores), p, False)
