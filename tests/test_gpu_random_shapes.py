@@ -439,3 +439,36 @@ def test_random_topk_many_short_rows(seed):
         run_topk(synth.bf16_bits_to_f32(bits), to_dev(bits), p, True)
     else:
         run_topk(x.scores, to_dev(x.scores), p, False)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prefill_many_tokens(seed):
+    """At least 512 (request, token) rows of at most 2048 blocks: the prompt
+    selects run in the narrow instances (512 threads, one key slot, or 256
+    threads in score order)."""
+    rng = np.random.default_rng(9700 + seed)
+    B = int(rng.integers(1, 4))
+    T = int(max(rng.integers(200, 701), -(-512 // B)))
+    H = int(rng.choice([1, 4]))
+    N_pad = int(rng.integers(1, 2049))
+    while B * T * N_pad * H > 8_000_000 and N_pad > 1:
+        N_pad //= 2
+    pos0 = [int([0, rng.integers(0, 16 * N_pad + 1), 16 * N_pad][int(rng.integers(3))])
+            for _ in range(B)]
+    K = int([1, rng.integers(2, 300), rng.integers(300, 1025)][int(rng.integers(3))])
+    srt = bool(rng.integers(2))
+    say(f"[random prefill many tokens {seed}] B={B} T={T} H={H} N_pad={N_pad} pos0={pos0} "
+        f"K={K} sorted={srt}")
+    x = synth.make_prefill(B, T, H, 128, N_pad, pos0, K, 9750 + seed, sorted_out=srt)
+    qd, cd, pd = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
+    ids = torch.full((B, T, K), POISON, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, T), POISON, dtype=torch.int32, device="cuda")
+    _, _, s = idx.idx_select_prefill(qd, cd, pd, K, sorted=srt, ids=ids, counts=cnt,
+                                     return_scores=True)
+    torch.cuda.synchronize()
+    R = B * T
+    s = s.cpu().numpy().reshape(R, -1)
+    S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+    S, A, NV = S.reshape(R, -1), A.reshape(R, -1), NV.reshape(R)
+    check_scores(s, S, A, RTOL[x.dtype])
+    check_ids_exact(ids.cpu().numpy().reshape(R, K), cnt.cpu().numpy().reshape(R), s, NV, K, srt)
