@@ -472,3 +472,40 @@ def test_random_prefill_many_tokens(seed):
     S, A, NV = S.reshape(R, -1), A.reshape(R, -1), NV.reshape(R)
     check_scores(s, S, A, RTOL[x.dtype])
     check_ids_exact(ids.cpu().numpy().reshape(R, K), cnt.cpu().numpy().reshape(R), s, NV, K, srt)
+
+
+def test_random_shapes_on_concurrent_streams():
+    """Calls of different shapes in flight together on four streams, each with
+    the binding's workspace of its own stream: every output equals the oracle's
+    (no state is shared between calls other than their workspaces)."""
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    jobs = []
+    for i, st in enumerate(streams):
+        p = draw_select(800 + i)
+        x = synth.make_indexer(p["B"], p["H"], 128, p["N_pad"], p["seq"], p["K"], p["dtype"],
+                               8800 + i, sorted_out=p["srt"], page_size=p["page"])
+        t = draw_topk(800 + i)
+        y = synth.make_topk(t["B"], t["N"], t["K"], 8900 + i)
+        q, c, sl, sc = to_dev(x.q), to_dev(x.c), to_dev(x.seq_len), to_dev(y.scores)
+        nvd = None if t["nv"] is None else torch.from_numpy(t["nv"]).to("cuda")
+        torch.cuda.synchronize()
+        jobs.append((p, x, q, c, sl, t, y, sc, nvd, st))
+    outs = []
+    for p, x, q, c, sl, t, y, sc, nvd, st in jobs:
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            a = idx.idx_select(q, c, sl, p["K"], page_size=p["page"], sorted=p["srt"],
+                               return_scores=True)
+            b = idx.idx_topk(sc, t["K"], nvd, t["srt"])
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for (p, x, q, c, sl, t, y, sc, nvd, st), (a, b) in zip(jobs, outs):
+        say(f"[concurrent] select B={p['B']} N_pad={p['N_pad']} K={p['K']}; "
+            f"topk B={t['B']} N={t['N']} K={t['K']}")
+        ids, counts, s = (v.cpu().numpy() for v in a)
+        S, A = oracle.score(x.q, x.c, x.seq_len, x.page_size, x.dtype)
+        check_scores(s, S, A, RTOL[x.dtype])
+        check_ids_exact(ids, counts, s, oracle.n_valid(x.seq_len, x.page_size, x.N_pad), p["K"],
+                        p["srt"])
+        nv = None if t["nv"] is None else np.clip(t["nv"], 0, t["N"])
+        check_ids_exact(b[0].cpu().numpy(), b[1].cpu().numpy(), y.scores, nv, t["K"], t["srt"])
