@@ -51,6 +51,9 @@ Other modes:
   --parse-trace DIR    per-workload kernel statistics of the timed regions from a
                        rocprofv3 --kernel-trace run of this script (the regions
                        are bracketed by empty marker launches)
+  --paged-sweep        idx_select_paged over the five page-count regimes x five
+                       batch sizes of the centroid-scorer sweep: steady and
+                       cold-isolated time per cell, ids checked (one JSON line)
 """
 from __future__ import annotations
 
@@ -981,6 +984,41 @@ def read_traffic(workload):
 
 
 # ----------------------------------------------------------------------------------------
+def paged_sweep(torch, idx, flush, steps=20):
+    """idx_select_paged over the scorer sweep of the centroid pages: five
+    page-count regimes x five batch sizes over one pool of 16384 rows, H = 4,
+    K = 256, bf16. Per cell: the steady per-call time (a graph of `steps` calls
+    on the same inputs, replayed; the pool stays cached, as it would across a
+    serving loop's calls) and one isolated call after the 1 GiB flush; ids
+    checked against the oracle's selection from the GPU's scores."""
+    import numpy as np
+    import synth
+    from tests.helpers import check_ids_exact
+    cells = []
+    for r, regime in enumerate(synth.PAGE_REGIMES):
+        for B in synth.PAGED_BATCHES:
+            x = synth.make_paged(B, 4, 128, synth.POOL_BLOCKS, regime, 256, "bf16",
+                                 600 + 10 * r + B, name=f"sweep_r{r}_b{B}")
+            wl = Paged(x, torch, idx)
+            g = capture(torch, wl.step, steps)
+            g.replay()
+            steady = min(replay_ms(torch, g, steps) for _ in range(3)) * 1e3
+            del g
+            iso = statistics.median(isolated_ms(torch, wl.step, flush, 8)) * 1e3
+            wl.poison_outputs()
+            wl.step(0)
+            torch.cuda.synchronize()
+            ids, counts = wl.timed_outputs()
+            check_ids_exact(ids, counts, wl.gpu_scores(), np.asarray(wl.nv), x.K, x.sorted)
+            cells.append({"regime": f"N({regime[0]},{regime[1]})", "B": B,
+                          "page_slots": wl.units, "steady_us": steady,
+                          "isolated_cold_us": iso,
+                          "page_slots_per_s": wl.units / (steady * 1e-6)})
+            log(f"[sweep] N{regime} B={B}: {wl.units} slots, steady {steady:.2f} us, "
+                f"isolated cold {iso:.2f} us")
+    return cells
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -998,6 +1036,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the steady, isolated, host end-to-end, sorted and floor figures")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--paged-sweep", action="store_true",
+                    help="time idx_select_paged over the 5 page-count regimes x 5 batch sizes")
     a = ap.parse_args()
 
     if a.parse_pmc:
@@ -1023,6 +1063,9 @@ def main():
         return 1
     torch.cuda.set_device(0)
     flush = Flusher(torch, idx)
+    if a.paged_sweep:
+        print(json.dumps({"paged_sweep": paged_sweep(torch, idx, flush)}))
+        return 0
     if a.pmc_calibrate:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
