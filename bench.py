@@ -54,6 +54,8 @@ Other modes:
   --paged-sweep        idx_select_paged over the five page-count regimes x five
                        batch sizes of the centroid-scorer sweep: steady and
                        cold-isolated time per cell, ids checked (one JSON line)
+  --decode-shapes      idx_select on the decode shapes the pages time (one request,
+                       4 fp32 heads, 751 / 2049 / 7501 blocks of 4 tokens, K = 256)
 """
 from __future__ import annotations
 
@@ -1019,6 +1021,40 @@ def paged_sweep(torch, idx, flush, steps=20):
     return cells
 
 
+def decode_shapes(torch, idx, flush, steps=20):
+    """idx_select on the decode shapes the pages time their Metal score + top-K
+    kernels at ("Round 18 Track C", section 3: pos0 3000, 8192 and 30000, one
+    query token): one request, 4 fp32 heads of 128 dims, 4-token blocks, so
+    751, 2049 and 7501 blocks; K = 256 (the pages do not state K; the tiny
+    fp32 configuration's). Steady and cold-isolated time, both output orders,
+    ids checked against the oracle's selection from the GPU's scores."""
+    import numpy as np
+    import synth
+    from tests.helpers import check_ids_exact
+    cells = []
+    for pos0 in (3000, 8192, 30000):
+        n_pad = -(-(pos0 + 1) // 4)
+        for srt in (False, True):
+            x = synth.make_indexer(1, 4, 128, n_pad, [pos0 + 1], 256, "f32", pos0 + int(srt),
+                                   sorted_out=srt, page_size=4, name=f"decode_pos{pos0}")
+            wl = Indexer(x, torch, idx)
+            g = capture(torch, wl.step, steps)
+            g.replay()
+            steady = min(replay_ms(torch, g, steps) for _ in range(3)) * 1e3
+            del g
+            iso = statistics.median(isolated_ms(torch, wl.step, flush, 8)) * 1e3
+            wl.poison_outputs()
+            wl.step(0)
+            torch.cuda.synchronize()
+            ids, counts = wl.timed_outputs()
+            check_ids_exact(ids, counts, wl.gpu_scores(), np.asarray(wl.nv), x.K, srt)
+            cells.append({"pos0": pos0, "blocks": n_pad, "sorted": srt, "steady_us": steady,
+                          "isolated_cold_us": iso})
+            log(f"[decode] pos0={pos0} ({n_pad} blocks) sorted={srt}: steady {steady:.2f} us, "
+                f"isolated cold {iso:.2f} us")
+    return cells
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1038,6 +1074,8 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--paged-sweep", action="store_true",
                     help="time idx_select_paged over the 5 page-count regimes x 5 batch sizes")
+    ap.add_argument("--decode-shapes", action="store_true",
+                    help="time idx_select on the pages' decode shapes (pos0 3000/8192/30000)")
     a = ap.parse_args()
 
     if a.parse_pmc:
@@ -1065,6 +1103,9 @@ def main():
     flush = Flusher(torch, idx)
     if a.paged_sweep:
         print(json.dumps({"paged_sweep": paged_sweep(torch, idx, flush)}))
+        return 0
+    if a.decode_shapes:
+        print(json.dumps({"decode_shapes": decode_shapes(torch, idx, flush)}))
         return 0
     if a.pmc_calibrate:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
