@@ -1052,6 +1052,27 @@ def decode_shapes(torch, idx, flush, steps=20):
                           "isolated_cold_us": iso})
             log(f"[decode] pos0={pos0} ({n_pad} blocks) sorted={srt}: steady {steady:.2f} us, "
                 f"isolated cold {iso:.2f} us")
+        # two and four query tokens (the page's ntok): idx_select_prefill, whose
+        # tokens are bf16 (the page's are fp32)
+        for ntok in (2, 4):
+            n_pad = -(-(pos0 + ntok) // 4)
+            x = synth.make_prefill(1, ntok, 4, 128, n_pad, [pos0], 256, pos0 + ntok,
+                                   page_size=4, name=f"prompt_pos{pos0}_ntok{ntok}")
+            wl = Prefill(x, torch, idx)
+            g = capture(torch, wl.step, steps)
+            g.replay()
+            steady = min(replay_ms(torch, g, steps) for _ in range(3)) * 1e3
+            del g
+            iso = statistics.median(isolated_ms(torch, wl.step, flush, 8)) * 1e3
+            wl.poison_outputs()
+            wl.step(0)
+            torch.cuda.synchronize()
+            outs = wl.timed_outputs()
+            wl.parity(outs, wl.gpu_scores())
+            cells.append({"pos0": pos0, "blocks": n_pad, "ntok": ntok, "inputs": "bf16",
+                          "steady_us": steady, "isolated_cold_us": iso})
+            log(f"[decode] pos0={pos0} ntok={ntok} (bf16 tokens): steady {steady:.2f} us, "
+                f"isolated cold {iso:.2f} us")
     return cells
 
 
