@@ -470,7 +470,7 @@ class Prefill(Workload):
         self.sorted_variant = not x.sorted
         self.ids = torch.empty(x.B, x.T, x.K, dtype=torch.int32, device="cuda")
         self.counts = torch.empty(x.B, x.T, dtype=torch.int32, device="cuda")
-        self.ws = torch.empty(idx.idx_prefill_workspace_bytes(x.B, x.T, x.N_pad, x.K, 0),
+        self.ws = torch.zeros(idx.idx_prefill_workspace_bytes(x.B, x.T, x.N_pad, x.K, 0),
                               dtype=torch.uint8, device="cuda")
         ps = x.page_size
         nv = [np.minimum(x.N_pad, (max(int(p), 0) + np.arange(x.T) + 1 + ps - 1) // ps)
@@ -1052,9 +1052,10 @@ def decode_shapes(torch, idx, flush, steps=20):
                           "isolated_cold_us": iso})
             log(f"[decode] pos0={pos0} ({n_pad} blocks) sorted={srt}: steady {steady:.2f} us, "
                 f"isolated cold {iso:.2f} us")
-        # two and four query tokens (the page's ntok): idx_select_prefill, whose
-        # tokens are bf16 (the page's are fp32)
-        for ntok in (2, 4):
+        # two and four query tokens (the page's ntok) and eight (the most one
+        # fused launch takes): idx_select_prefill, whose tokens are bf16 (the
+        # page's are fp32)
+        for ntok in (2, 4, 8):
             n_pad = -(-(pos0 + ntok) // 4)
             x = synth.make_prefill(1, ntok, 4, 128, n_pad, [pos0], 256, pos0 + ntok,
                                    page_size=4, name=f"prompt_pos{pos0}_ntok{ntok}")

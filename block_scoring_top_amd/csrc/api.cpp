@@ -353,11 +353,21 @@ int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_p
                                            dt == IDX_BF16, stream));
 }
 
+// Prompt-token calls of a few tokens over few rows run as one fused select per
+// token row (each row reads its request's table; the heads are not summed
+// first); longer prompts go through the matrix-core scores and a top-K.
+constexpr int kPrefillFusedMaxTokens = 8;
+constexpr int kPrefillFusedMaxRows = 256;
+// arrival lines of the fused rows, at a fixed place so that calls of any shape
+// can share one workspace; then the per-token counts, then the score staging
+constexpr size_t kPrefillTicketBytes = kPrefillFusedMaxRows * size_t(128);
+
 size_t idx_prefill_workspace_bytes(int B, int T, int N_pad, int K, uint32_t flags) {
   (void)K; (void)flags;
   if (B < 1 || T < 1 || N_pad < 1) return 0;
   const size_t rows = (size_t)B * T;
-  return round_up(rows * sizeof(int32_t), 256) + rows * stage_stride(N_pad) * sizeof(float);
+  return kPrefillTicketBytes + round_up(rows * sizeof(int32_t), 256) +
+         rows * stage_stride(N_pad) * sizeof(float);
 }
 
 int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_t* ids,
@@ -383,12 +393,21 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
   if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
   const size_t need = idx_prefill_workspace_bytes(B, T, N_pad, K, flags);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return IDX_ERR_WORKSPACE;
-  int32_t* n_valid = static_cast<int32_t*>(ws);
+  char* w = static_cast<char*>(ws);
+  int32_t* n_valid = reinterpret_cast<int32_t*>(w + kPrefillTicketBytes);
+  float* stage = reinterpret_cast<float*>(w + kPrefillTicketBytes +
+                                          round_up((size_t)rows * sizeof(int32_t), 256));
+  if (T <= kPrefillFusedMaxTokens && rows <= kPrefillFusedMaxRows && rows * N_pad <= kMaxRows) {
+    const SelectLaunch L = resolve_select((int)rows, H, N_pad, page_size, K, IDX_BF16,
+                                          flags & IDX_SORTED);
+    return hip_status(idxk::launch_select_tokens(
+        q, c, pos0, ids, counts, scores_out, (int)rows, T, H, N_pad, page_size, K, sorted,
+        L.chunk, L.wide, reinterpret_cast<uint32_t*>(w), stage, stage_stride(N_pad), stream));
+  }
   float* scores = scores_out;
   int64_t stride = N_pad;
   if (scores == nullptr) {  // staged in the workspace, rows 16-byte aligned
-    scores = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                      round_up((size_t)rows * sizeof(int32_t), 256));
+    scores = stage;
     stride = stage_stride(N_pad);
   }
   // staged scores are read only up to each token's count: no -inf fill

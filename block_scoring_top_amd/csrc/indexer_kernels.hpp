@@ -148,6 +148,10 @@ constexpr int kPageStage = 256;  // page-list entries a paged chunk stages in LD
 // PAGED: request b's score slots are its page list indices[indptr[b] ..
 // indptr[b+1]) (at most N_pad of them) into a shared pool of n_rows centroids;
 // otherwise its N_pad rows of c, the first n_valid(seq_len[b]) of them scored.
+// tokens > 0 (query tokens of a prompt): row b is token b % tokens of request
+// b / tokens, whose table it scores; seq_len then holds each request's first
+// position pos0, and the token at pos0 + t sees the blocks n < n_valid(pos0 +
+// t + 1) (negative pos0 counts as 0).
 // R8: 8-bit radix digits, no linear-bin pass (dense tables; the same results).
 template <bool BF16, bool SORTED, int NT, int SLOTS, bool BLOCKED, bool PAGED, bool R8 = false>
 __global__ __launch_bounds__(NT) void select_fused_kernel(
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
     int32_t* __restrict__ ids, int32_t* __restrict__ counts, float* __restrict__ scores_out,
     int H, int N_pad, int page_size, int K, int chunk, int nchunk, uint32_t* tickets,
     float* stage, int stage_stride, const int32_t* __restrict__ indptr,
-    const int32_t* __restrict__ indices, int64_t n_indices, int n_rows) {
+    const int32_t* __restrict__ indices, int64_t n_indices, int n_rows, int tokens) {
   __shared__ SelectSmem<NT, SLOTS> sm;
   __shared__ int s_last;
   __shared__ int32_t s_pages[PAGED ? kPageStage : 1];
@@ -168,11 +172,17 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
   qh.issue(q, b, H, 0, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
   int nv;
   int64_t pbase = 0, avail = 0;
+  int tb = b;  // the centroid table this row scores
   if constexpr (PAGED) {
     const int lo = indptr[b], hi = indptr[b + 1];
     nv = min(max(hi - lo, 0), N_pad);
     pbase = lo;
     avail = (lo >= 0 && (int64_t)lo < n_indices) ? n_indices - lo : 0;
+  } else if (tokens > 0) {
+    tb = b / tokens;
+    const int64_t seen = (int64_t)max(seq_len[tb], 0) + (b - tb * tokens) + 1;
+    const int64_t nb = (seen + page_size - 1) / page_size;
+    nv = (int)(nb < N_pad ? nb : N_pad);
   } else {
     nv = n_valid_blocks(seq_len[b], page_size, N_pad);
   }
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(NT) void select_fused_kernel(
         score_rows<BF16, NT, true, U>(c, StagedRows{s_pages, s0}, qh, q, b, H, s0, s1, row);
       }
     } else
-      score_rows<BF16, NT, true, U>(table_of<BF16>(c, (size_t)b * N_pad), DenseRows{}, qh, q, b,
+      score_rows<BF16, NT, true, U>(table_of<BF16>(c, (size_t)tb * N_pad), DenseRows{}, qh, q, b,
                                     H, r0, r1, row);
   }
   if (scores_out != nullptr) fill_neg_inf(row, max(r0, nv), r_end);
@@ -319,7 +329,7 @@ int launch_select_t(const void* q, const void* c, const int32_t* seq_len, int32_
                     int32_t* counts, float* scores_out, int B, int H, int N_pad, int page_size,
                     int K, bool bf16, bool sorted, int chunk, bool wide, uint32_t* tickets,
                     float* stage, int stage_stride, const int32_t* indptr, const int32_t* indices,
-                    int64_t n_indices, int n_rows, void* stream) {
+                    int64_t n_indices, int n_rows, void* stream, int tokens = 0) {
   const int nchunk = (N_pad + chunk - 1) / chunk;
   const dim3 grid((unsigned)B * nchunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -338,14 +348,14 @@ int launch_select_t(const void* q, const void* c, const int32_t* seq_len, int32_
         hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL, true>), grid, dim3(NT_), \
                            SO ? sort_lds_bytes(K) : 0, s, q, c, seq_len, ids, counts,          \
                            scores_out, H, N_pad, page_size, K, chunk, nchunk, tickets, stage,  \
-                           stage_stride, indptr, indices, n_indices, n_rows);                  \
+                           stage_stride, indptr, indices, n_indices, n_rows, 0);               \
         break;                                                                                 \
       }                                                                                        \
     }                                                                                          \
     hipLaunchKernelGGL((select_fused_kernel<BF, SO, NT_, SL_, BL, false, R8>), grid,           \
                        dim3(NT_), SO ? sort_lds_bytes(K) : 0, s, q, c, seq_len, ids, counts,   \
                        scores_out, H, N_pad, page_size, K, chunk, nchunk, tickets, stage,      \
-                       stage_stride, indptr, indices, n_indices, n_rows);                      \
+                       stage_stride, indptr, indices, n_indices, n_rows, tokens);              \
   } while (0)
 #define IDX_LAUNCH_FUSED_NT(BF, SO)                                                  \
   if (wide) {                                                                        \

@@ -38,8 +38,9 @@
  *     returns to zero, and scratch, which calls overwrite before reading. One
  *     workspace may serve any sequence of calls on one stream whose sizes come
  *     from the same *_workspace_bytes() function (idx_select, idx_select_paged
- *     and plans share one layout, idx_topk and idx_topk_bf16 another; the
- *     layouts differ, so a buffer used under one must be zero-filled again
+ *     and plans share one layout, idx_topk and idx_topk_bf16 another,
+ *     idx_select_prefill a third; the layouts differ, so a buffer used under
+ *     one must be zero-filled again
  *     before it serves another). Calls that may overlap (other streams) need
  *     distinct workspaces.
  */
@@ -287,13 +288,16 @@ int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_p
  * Each (b, t) row then gets the selection of idx_topk:
  *   ids        [B,T,K] int32 output;  counts [B,T] int32 output or NULL
  *   scores_out [B,T,N_pad] float32 output or NULL (16-byte aligned)
- * The heads are summed per token in fp32 and split into two bf16 parts for
- * the matrix cores (the dropped remainder is below 2^-16 of each summed
- * value), products accumulated in fp32.
+ * Calls with T <= 8 and B*T <= 256 score each token row as idx_select does
+ * (one fused launch; products and head sums in fp32). Longer prompts sum the
+ * heads per token in fp32 and split the sum into two bf16 parts for the
+ * matrix cores (the dropped remainder is below 2^-16 of each summed value),
+ * products accumulated in fp32; the top-K follows in a second launch.
  * dt == IDX_BF16, D == IDX_HEAD_DIM, H <= IDX_MAX_HEADS, K >= 1 (K <=
  * IDX_MAX_SORTED_K with IDX_SORTED).
  * ws / ws_bytes: at least idx_prefill_workspace_bytes(B, T, N_pad, K, flags)
- * bytes (no zero-fill needed): per-token block counts and score staging.
+ * bytes, zero-filled before first use: arrival lines (left zeroed by each
+ * call), then per-token block counts and score staging.
  */
 size_t idx_prefill_workspace_bytes(int B, int T, int N_pad, int K, uint32_t flags);
 int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_t* ids,

@@ -250,9 +250,10 @@ def test_select_prefill_rejects(lib, kw, want):
 
 
 def test_prefill_workspace_size(lib):
-    # per-token block counts (256-byte aligned), then B*T staged rows of round_up(N_pad, 4)
-    assert lib.idx_prefill_workspace_bytes(2, 64, 500, 10, 0) == 512 + 128 * 500 * 4
-    assert lib.idx_prefill_workspace_bytes(1, 3, 7, 10, 0) == 256 + 3 * 8 * 4
+    # 256 arrival lines of 128 bytes, per-token block counts (256-byte aligned),
+    # then B*T staged rows of round_up(N_pad, 4)
+    assert lib.idx_prefill_workspace_bytes(2, 64, 500, 10, 0) == 256 * 128 + 512 + 128 * 500 * 4
+    assert lib.idx_prefill_workspace_bytes(1, 3, 7, 10, 0) == 256 * 128 + 256 + 3 * 8 * 4
     assert lib.idx_prefill_workspace_bytes(0, 3, 7, 10, 0) == 0
 
 

@@ -164,23 +164,24 @@ def test_graph_paged_against_oracle():
                     [ids, counts, s], check)
 
 
-def test_graph_prefill_against_oracle():
-    x = synth.make_prefill(2, 100, 4, 128, 600, [2000, 7000], 64, 902)
+@pytest.mark.parametrize("T", [100, 4])   # matrix-core scores + top-K; one fused launch
+def test_graph_prefill_against_oracle(T):
+    x = synth.make_prefill(2, T, 4, 128, 600, [2000, 7000], 64, 902)
     q, c, p0 = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
-    ids = torch.empty(2, 100, 64, dtype=torch.int32, device="cuda")
-    counts = torch.empty(2, 100, dtype=torch.int32, device="cuda")
-    s = torch.empty(2, 100, 600, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(idx.idx_prefill_workspace_bytes(2, 100, 600, 64, 1), dtype=torch.uint8,
+    ids = torch.empty(2, T, 64, dtype=torch.int32, device="cuda")
+    counts = torch.empty(2, T, dtype=torch.int32, device="cuda")
+    s = torch.empty(2, T, 600, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(idx.idx_prefill_workspace_bytes(2, T, 600, 64, 1), dtype=torch.uint8,
                      device="cuda")
     S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, 16, "bf16")
-    R = 200
+    R = 2 * T
 
     def check(ids_h, counts_h, s_h):
         sh = s_h.reshape(R, -1)
         check_scores(sh, S.reshape(R, -1), A.reshape(R, -1), RTOL["bf16"])
         check_ids_exact(ids_h.reshape(R, -1), counts_h.reshape(R), sh, NV.reshape(R), 64, True)
 
-    replays_checked("prefill", lambda: idx.idx_select_prefill(q, c, p0, 64, sorted=True, ids=ids,
+    replays_checked(f"prefill T={T}", lambda: idx.idx_select_prefill(q, c, p0, 64, sorted=True, ids=ids,
                                                               counts=counts, scores_out=s, ws=ws),
                     [ids, counts, s], check)
 

@@ -87,3 +87,62 @@ def test_prefill_workload_full_size():
     x = synth.workload(7)
     full_prefill_check(x)
     full_prefill_check(x, sorted_out=True)
+
+
+# ---- a few tokens over few rows: one fused score + select launch per call ----------------
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("sorted_out", [False, True])
+def test_prefill_few_tokens(T, sorted_out):
+    """The short-prompt route (T <= 8, B*T <= 256): starts at 0, inside a page,
+    negative, and past the table (every block visible), ragged table length."""
+    x = synth.make_prefill(5, T, 4, 128, 1537, [0, 333, -9, 24570, 30000], 100, 710 + T,
+                           name=f"few_T{T}")
+    full_prefill_check(x, sorted_out=sorted_out)
+
+
+@pytest.mark.parametrize("H", [1, 4, 16])
+def test_prefill_few_tokens_integer_inputs_bit_exact(H):
+    """Small integers on the short-prompt route: every product and head sum is
+    an exact integer in fp32, so the scores equal the oracle's exactly."""
+    x = synth.make_prefill(3, 4, H, 128, 300, [1000, 2500, 5], 32, 720 + H, integer=True,
+                           name=f"few_integer_H{H}")
+    full_prefill_check(x, exact_scores=True)
+
+
+@pytest.mark.parametrize("B,T", [(32, 8), (33, 8), (1, 9), (128, 2), (129, 2)])
+def test_prefill_route_boundaries(B, T):
+    """Both sides of the short-prompt limits (B*T = 256 fused, 257 or T = 9 not),
+    checked against the oracle the same way."""
+    rng = np.random.default_rng(730 + B * T)
+    x = synth.make_prefill(B, T, 4, 128, 700, rng.integers(-20, 12000, B), 64, 731 + B,
+                           name=f"route_B{B}_T{T}")
+    full_prefill_check(x, sorted_out=bool(B & 1))
+
+
+def test_prefill_workspace_shared_by_both_routes():
+    """One zero-filled workspace serves short and long prompts in turn (its
+    arrival lines sit at a fixed place whatever the call's shape)."""
+    shapes = [(20, 8, 900, 37), (3, 70, 900, 200), (64, 4, 500, 256), (2, 40, 1300, 30),
+              (64, 4, 500, 256), (1, 1, 1300, 5)]
+    nbytes = max(idx.idx_prefill_workspace_bytes(B, T, N, K) for B, T, N, K in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for i, (B, T, N, K) in enumerate(shapes):
+        rng = np.random.default_rng(740 + i)
+        x = synth.make_prefill(B, T, 4, 128, N, rng.integers(-5, N * 16, B), K, 740 + i)
+        say(f"[prefill shared ws] B={B} T={T} N_pad={N} K={K}")
+        ids, counts, s = idx.idx_select_prefill(to_dev(x.q), to_dev(x.c), to_dev(x.pos0), K,
+                                                sorted=bool(i & 1), return_scores=True, ws=ws)
+        torch.cuda.synchronize()
+        S, A, NV = oracle.score_prefill(x.q, x.c, x.pos0, x.page_size, x.dtype)
+        R = B * T
+        s2 = s.cpu().numpy().reshape(R, -1)
+        check_scores(s2, S.reshape(R, -1), A.reshape(R, -1), RTOL["bf16"])
+        check_ids_exact(ids.cpu().numpy().reshape(R, K), counts.cpu().numpy().reshape(R), s2,
+                        NV.reshape(R), K, bool(i & 1))
+
+
+@pytest.mark.parametrize("page_size", [1, 5, 64])
+def test_prefill_few_tokens_page_sizes(page_size):
+    x = synth.make_prefill(3, 3, 4, 128, 900, [0, 61, 2 * 900 * page_size], 50, 750 + page_size,
+                           page_size=page_size, name=f"few_page{page_size}")
+    full_prefill_check(x)
