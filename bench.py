@@ -479,7 +479,8 @@ class Prefill(Workload):
         rows = sum(int(v.max()) for v in nv)                    # centroid rows any token sees
         # centroid rows read + query heads + pos0 + ids written (the per-token
         # score rows are an intermediate and are not credited)
-        self.alg_bytes = rows * 256 + x.q.size * 2 + 4 * x.B + 4 * x.B * x.T * x.K
+        esz = 4 if x.dtype == "f32" else 2
+        self.alg_bytes = rows * 128 * esz + x.q.size * esz + 4 * x.B + 4 * x.B * x.T * x.K
         self.alg_flops = 2 * self.units * 128
 
     def step(self, i, sorted=None):
@@ -503,7 +504,13 @@ class Prefill(Workload):
         return {"workload": x.name, "call": "idx_select_prefill", "B": x.B, "T": x.T, "H": x.H,
                 "D": 128, "N_pad": x.N_pad, "pos0": [int(v) for v in x.pos0],
                 "page_size": x.page_size, "K": x.K, "sorted": x.sorted, "inputs": x.dtype,
-                "accumulate": "f32 (MFMA)", "token_block_pairs": self.units}
+                "accumulate": "f32" if self.fused_route() else "f32 (MFMA)",
+                "token_block_pairs": self.units}
+
+    def fused_route(self):
+        """Calls of at most 8 tokens and 256 token rows: one fused select."""
+        x = self.x
+        return x.T <= 8 and x.B * x.T <= 256 and x.B * x.T * x.N_pad < 2 ** 31
 
     def oracle_call(self, i):
         import oracle
@@ -1053,11 +1060,10 @@ def decode_shapes(torch, idx, flush, steps=20):
             log(f"[decode] pos0={pos0} ({n_pad} blocks) sorted={srt}: steady {steady:.2f} us, "
                 f"isolated cold {iso:.2f} us")
         # two and four query tokens (the page's ntok) and eight (the most one
-        # fused launch takes): idx_select_prefill, whose tokens are bf16 (the
-        # page's are fp32)
+        # fused launch takes): idx_select_prefill, fp32 like the page's
         for ntok in (2, 4, 8):
             n_pad = -(-(pos0 + ntok) // 4)
-            x = synth.make_prefill(1, ntok, 4, 128, n_pad, [pos0], 256, pos0 + ntok,
+            x = synth.make_prefill(1, ntok, 4, 128, n_pad, [pos0], 256, pos0 + ntok, dtype="f32",
                                    page_size=4, name=f"prompt_pos{pos0}_ntok{ntok}")
             wl = Prefill(x, torch, idx)
             g = capture(torch, wl.step, steps)
@@ -1070,9 +1076,9 @@ def decode_shapes(torch, idx, flush, steps=20):
             torch.cuda.synchronize()
             outs = wl.timed_outputs()
             wl.parity(outs, wl.gpu_scores())
-            cells.append({"pos0": pos0, "blocks": n_pad, "ntok": ntok, "inputs": "bf16",
+            cells.append({"pos0": pos0, "blocks": n_pad, "ntok": ntok, "inputs": "f32",
                           "steady_us": steady, "isolated_cold_us": iso})
-            log(f"[decode] pos0={pos0} ntok={ntok} (bf16 tokens): steady {steady:.2f} us, "
+            log(f"[decode] pos0={pos0} ntok={ntok}: steady {steady:.2f} us, "
                 f"isolated cold {iso:.2f} us")
     return cells
 

@@ -388,7 +388,11 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
   if (rows > kMaxRows || rows * N_pad > (int64_t(1) << 40) || rows * K > kMaxRows ||
       (int64_t)B * N_pad > kMaxRows)
     return IDX_ERR_INVALID_ARG;
-  if (dt != IDX_BF16 || H > IDX_MAX_HEADS || D != IDX_HEAD_DIM) return IDX_ERR_UNSUPPORTED;
+  // a few tokens over few rows: one fused select over the token rows
+  const bool fused =
+      T <= kPrefillFusedMaxTokens && rows <= kPrefillFusedMaxRows && rows * N_pad <= kMaxRows;
+  if ((dt != IDX_BF16 && !fused) || H > IDX_MAX_HEADS || D != IDX_HEAD_DIM)
+    return IDX_ERR_UNSUPPORTED;
   const bool sorted = (flags & IDX_SORTED) != 0;
   if (sorted && K > IDX_MAX_SORTED_K) return IDX_ERR_UNSUPPORTED;
   const size_t need = idx_prefill_workspace_bytes(B, T, N_pad, K, flags);
@@ -397,12 +401,13 @@ int idx_select_prefill(const void* q, const void* c, const int32_t* pos0, int32_
   int32_t* n_valid = reinterpret_cast<int32_t*>(w + kPrefillTicketBytes);
   float* stage = reinterpret_cast<float*>(w + kPrefillTicketBytes +
                                           round_up((size_t)rows * sizeof(int32_t), 256));
-  if (T <= kPrefillFusedMaxTokens && rows <= kPrefillFusedMaxRows && rows * N_pad <= kMaxRows) {
-    const SelectLaunch L = resolve_select((int)rows, H, N_pad, page_size, K, IDX_BF16,
+  if (fused) {
+    const SelectLaunch L = resolve_select((int)rows, H, N_pad, page_size, K, dt,
                                           flags & IDX_SORTED);
     return hip_status(idxk::launch_select_tokens(
-        q, c, pos0, ids, counts, scores_out, (int)rows, T, H, N_pad, page_size, K, sorted,
-        L.chunk, L.wide, reinterpret_cast<uint32_t*>(w), stage, stage_stride(N_pad), stream));
+        q, c, pos0, ids, counts, scores_out, (int)rows, T, H, N_pad, page_size, K, L.bf16,
+        sorted, L.chunk, L.wide, reinterpret_cast<uint32_t*>(w), stage, stage_stride(N_pad),
+        stream));
   }
   float* scores = scores_out;
   int64_t stride = N_pad;

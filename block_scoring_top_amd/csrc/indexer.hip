@@ -130,12 +130,12 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
 
 int launch_select_tokens(const void* q, const void* c, const int32_t* pos0, int32_t* ids,
                          int32_t* counts, float* scores_out, int B, int tokens, int H, int N_pad,
-                         int page_size, int K, bool sorted, int chunk, bool wide,
+                         int page_size, int K, bool bf16, bool sorted, int chunk, bool wide,
                          uint32_t* tickets, float* stage, int stage_stride, void* stream) {
   if (tokens < 1) return (int)hipErrorInvalidValue;
   return launch_select_t<false>(q, c, pos0, ids, counts, scores_out, B, H, N_pad, page_size, K,
-                                /*bf16=*/true, sorted, chunk, wide, tickets, stage, stage_stride,
-                                nullptr, nullptr, 0, 0, stream, tokens);
+                                bf16, sorted, chunk, wide, tickets, stage, stage_stride, nullptr,
+                                nullptr, 0, 0, stream, tokens);
 }
 
 // ---- static scratch of idx_select_noalloc ------------------------------------------------

@@ -45,7 +45,7 @@ int launch_select(const void* q, const void* c, const int32_t* seq_len, int32_t*
 // request), seq_len the requests' first positions.
 int launch_select_tokens(const void* q, const void* c, const int32_t* pos0, int32_t* ids,
                          int32_t* counts, float* scores_out, int B, int tokens, int H, int N_pad,
-                         int page_size, int K, bool sorted, int chunk, bool wide,
+                         int page_size, int K, bool bf16, bool sorted, int chunk, bool wide,
                          uint32_t* tickets, float* stage, int stage_stride, void* stream);
 int launch_select_radix8(const void* q, const void* c, const int32_t* seq_len, int32_t* ids,
                          int32_t* counts, float* scores_out, int B, int H, int N_pad,

@@ -278,9 +278,9 @@ int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_p
  * scores tiles of query tokens against the block keys with a matrix product,
  * every token before its top-K; "Round 18 Track C", section 3: the score
  * stage grows with the number of query tokens).
- *   q    [B,T,H,D] bf16 (16-byte aligned): token t of request b sits at
- *        position pos0[b] + t
- *   c    [B,N_pad,D] bf16 (16-byte aligned): the request's block centroids
+ *   q    [B,T,H,D] (16-byte aligned): token t of request b sits at position
+ *        pos0[b] + t
+ *   c    [B,N_pad,D] (16-byte aligned): the request's block centroids
  *   pos0 [B] int32 device array (negative values count as 0)
  * Token t sees the blocks n < n_valid = min(N_pad, ceil((pos0[b] + t + 1) /
  * page_size)) (the blocks up to the one holding itself), and
@@ -288,13 +288,14 @@ int idx_pool_keys(const void* k, const int32_t* seq_len, void* c, int B, int S_p
  * Each (b, t) row then gets the selection of idx_topk:
  *   ids        [B,T,K] int32 output;  counts [B,T] int32 output or NULL
  *   scores_out [B,T,N_pad] float32 output or NULL (16-byte aligned)
- * Calls with T <= 8 and B*T <= 256 score each token row as idx_select does
- * (one fused launch; products and head sums in fp32). Longer prompts sum the
- * heads per token in fp32 and split the sum into two bf16 parts for the
- * matrix cores (the dropped remainder is below 2^-16 of each summed value),
- * products accumulated in fp32; the top-K follows in a second launch.
- * dt == IDX_BF16, D == IDX_HEAD_DIM, H <= IDX_MAX_HEADS, K >= 1 (K <=
- * IDX_MAX_SORTED_K with IDX_SORTED).
+ * Calls with T <= 8, B*T <= 256 and B*T*N_pad < 2^31 score each token row as
+ * idx_select does (one fused launch; products and head sums in fp32), with
+ * fp32 or bf16 inputs. Longer prompts (bf16 only) sum the heads per token in
+ * fp32 and split the sum into two bf16 parts for the matrix cores (the
+ * dropped remainder is below 2^-16 of each summed value), products
+ * accumulated in fp32; the top-K follows in a second launch.
+ * dt == IDX_BF16 (or IDX_F32 on the short route), D == IDX_HEAD_DIM,
+ * H <= IDX_MAX_HEADS, K >= 1 (K <= IDX_MAX_SORTED_K with IDX_SORTED).
  * ws / ws_bytes: at least idx_prefill_workspace_bytes(B, T, N_pad, K, flags)
  * bytes, zero-filled before first use: arrival lines (left zeroed by each
  * call), then per-token block counts and score staging.

@@ -244,6 +244,9 @@ def prefill_call(lib, **kw):
     (dict(D=64), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(K=5000, flags=1), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(ws=P, ws_bytes=64), WORKSPACE), (dict(ws=P + 64), WORKSPACE),
     (dict(flags=2), UNSUPPORTED), (dict(flags=3), UNSUPPORTED),  # IDX_RADIX8
+    # fp32 inputs only on the short-prompt route (T <= 8, B*T <= 256)
+    (dict(dt=0, T=4), WORKSPACE), (dict(dt=0, B=32, T=8), WORKSPACE),
+    (dict(dt=0, B=33, T=8), UNSUPPORTED), (dict(dt=0, B=1, T=9), UNSUPPORTED),
 ])
 def test_select_prefill_rejects(lib, kw, want):
     assert prefill_call(lib, **kw) == want

@@ -146,3 +146,17 @@ def test_prefill_few_tokens_page_sizes(page_size):
     x = synth.make_prefill(3, 3, 4, 128, 900, [0, 61, 2 * 900 * page_size], 50, 750 + page_size,
                            page_size=page_size, name=f"few_page{page_size}")
     full_prefill_check(x)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_prefill_few_tokens_f32(T):
+    """fp32 inputs, which the short-prompt route takes (fp32 products and sums)."""
+    x = synth.make_prefill(4, T, 4, 128, 1100, [0, 97, -3, 20000], 128, 760 + T, dtype="f32",
+                           name=f"few_f32_T{T}")
+    full_prefill_check(x, sorted_out=T == 3)
+
+
+def test_prefill_f32_long_prompt_unsupported():
+    x = synth.make_prefill(1, 9, 4, 128, 64, [0], 8, 770, dtype="f32")
+    with pytest.raises(idx.IdxError):
+        run_prefill(x)

@@ -219,9 +219,10 @@ def test_random_prefill_shapes(seed):
             for _ in range(B)]
     K = int([1, rng.integers(1, 300), rng.integers(300, 1500)][int(rng.integers(3))])
     srt = bool(rng.integers(2))
+    dt = "f32" if T <= 8 and rng.integers(2) else "bf16"   # fp32: short prompts only
     say(f"[random prefill {seed}] B={B} T={T} H={H} N_pad={N_pad} pos0={pos0} K={K} "
-        f"sorted={srt}")
-    x = synth.make_prefill(B, T, H, 128, N_pad, pos0, K, 9600 + seed, sorted_out=srt)
+        f"sorted={srt} {dt}")
+    x = synth.make_prefill(B, T, H, 128, N_pad, pos0, K, 9600 + seed, dtype=dt, sorted_out=srt)
     qd, cd, pd = to_dev(x.q), to_dev(x.c), to_dev(x.pos0)
     ids = torch.full((B, T, K), POISON, dtype=torch.int32, device="cuda")
     cnt = torch.full((B, T), POISON, dtype=torch.int32, device="cuda")
