@@ -30,16 +30,27 @@ int chunk_rows(int B, int N_pad, uint32_t flags, int lo, int target) {
 }
 // idx_score: 256-thread workgroups, 16 rows per step, ~1024 of them (4 per CU)
 constexpr int kScoreChunkMin = 16, kScoreTarget = 1024;
-// idx_select: few requests -> 1024-thread workgroups (64 rows per step, ~256 of
-// them: one per CU, all resident at once; chunks of at least 32 rows, so that
-// small calls spread over more CUs: the tiny score-ordered call of 1024
-// blocks took 7.8 us with 64-row chunks, 7.55 with 32, 7.9 with 16); many
-// requests -> 512-thread workgroups (16 rows per step, ~1024)
+// idx_select: many requests -> 512-thread workgroups (16 rows per step, ~1024)
 constexpr int kWideMaxRequests = 32;
 // largest score-ordered K that the many-request workgroups (512 threads) sort
 // (kept at four ids per thread of a 256-thread workgroup)
 constexpr int kNarrowMaxSortedK = 1024;
-constexpr int kWideChunkMin = 32, kWideTarget = 256;
+// idx_select, few requests: 1024-thread workgroups, which score 64 rows per
+// step. A chunk of 32 rows leaves half of one idle, so it pays only while it
+// spreads the call over more CUs (the tiny score-ordered call of 1024 blocks:
+// 7.8 us with 64-row chunks, 7.55 with 32, 7.9 with 16). The chunk is the
+// smallest (32..256 rows) whose grid fits one workgroup per CU: with two per
+// CU two requests of 7501 blocks took 13.3 us (32-row chunks, 469 workgroups)
+// against 10.4 (64 rows, 235), and eight such requests in bf16 13.1 us against
+// 11.9 (128 and 256 rows).
+constexpr int kWideChunkMin = 32, kWideMaxGrid = 256;
+int chunk_rows_wide(int B, int N_pad, uint32_t flags) {
+  const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
+  if (l != 0) return 1 << l;
+  int c = kWideChunkMin;
+  while (c < 256 && (int64_t)B * ((N_pad + c - 1) / c) > kWideMaxGrid) c *= 2;
+  return c;
+}
 
 int check_chunk_flag(uint32_t flags) {
   const uint32_t l = (flags & IDX_CHUNK_MASK) >> IDX_CHUNK_SHIFT;
@@ -204,7 +215,7 @@ SelectLaunch resolve_select(int B, int H, int N_pad, int page_size, int K, idx_d
                             uint32_t flags) {
   const bool sorted = (flags & IDX_SORTED) != 0;
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
-  const int chunk = wide ? chunk_rows(B, N_pad, flags, kWideChunkMin, kWideTarget)
+  const int chunk = wide ? chunk_rows_wide(B, N_pad, flags)
                          : chunk_rows(B, N_pad, flags, kScoreChunkMin, kScoreTarget);
   return SelectLaunch{B,     H,      N_pad, page_size, K, dt == IDX_BF16, sorted, wide, chunk,
                       (flags & IDX_RADIX8) != 0};
@@ -333,7 +344,7 @@ int idx_select_paged(const void* q, const void* c_pool, const int32_t* kv_indptr
   uint32_t* tickets = static_cast<uint32_t*>(ws);
   float* stage = reinterpret_cast<float*>(static_cast<char*>(ws) + kTicketBytes);
   const bool wide = B <= kWideMaxRequests || (sorted && K > kNarrowMaxSortedK);
-  const int chunk = wide ? chunk_rows(B, max_pages, flags, kWideChunkMin, kWideTarget)
+  const int chunk = wide ? chunk_rows_wide(B, max_pages, flags)
                          : chunk_rows(B, max_pages, flags, kScoreChunkMin, kScoreTarget);
   return hip_status(idxk::launch_select(q, c_pool, nullptr, ids, counts, scores_out, B, H,
                                         max_pages, 1, K, dt == IDX_BF16, sorted, chunk, wide,
