@@ -160,3 +160,12 @@ def test_prefill_f32_long_prompt_unsupported():
     x = synth.make_prefill(1, 9, 4, 128, 64, [0], 8, 770, dtype="f32")
     with pytest.raises(idx.IdxError):
         run_prefill(x)
+
+
+@pytest.mark.parametrize("sorted_out", [False, True])
+def test_prefill_few_tokens_long_rows(sorted_out):
+    """The short-prompt route past the select's register tile (rows of more than
+    8192 blocks) with K = 2048, and tokens on both sides of a block boundary."""
+    x = synth.make_prefill(2, 3, 4, 128, 20000, [16 * 15000 - 2, 16 * 20000], 2048, 780,
+                           name="few_long")
+    full_prefill_check(x, sorted_out=sorted_out)
