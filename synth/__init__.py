@@ -114,17 +114,19 @@ def _normal_f32(rng, shape):
 
 
 def _poison_tail(c_bits: np.ndarray, seq_len: np.ndarray, page_size: int):
-    """Fill centroid rows past each request's last page with a bf16 NaN pattern,
-    so that any read of a masked row shows up in a result."""
+    """Fill centroid rows past each request's last page with NaN (a bf16 NaN
+    pattern for bf16 bits, a float NaN for fp32), so that any read of a masked
+    row shows up in a result."""
     n_pad = c_bits.shape[1]
+    fill = np.float32(np.nan) if c_bits.dtype == np.float32 else BF16_POISON
     for b, s in enumerate(seq_len):
         nv = min(n_pad, -(-int(s) // page_size))
-        c_bits[b, nv:, :] = BF16_POISON
+        c_bits[b, nv:, :] = fill
 
 
 def make_indexer(B, H, D, N_pad, seq_len, K, dtype, seed, sorted_out=False,
                  page_size=PAGE_SIZE, name="custom", poison=True):
-    """q and c i.i.d. N(0,1) (fp32, or rounded to bf16); padded tail poisoned (bf16)."""
+    """q and c i.i.d. N(0,1) (fp32, or rounded to bf16); padded tail poisoned."""
     rng = np.random.default_rng(seed)
     seq_len = np.asarray(seq_len, dtype=np.int64)
     if seq_len.ndim == 0:
@@ -134,8 +136,8 @@ def make_indexer(B, H, D, N_pad, seq_len, K, dtype, seed, sorted_out=False,
     if dtype == "bf16":
         q = f32_to_bf16_bits(q)
         c = f32_to_bf16_bits(c)
-        if poison:
-            _poison_tail(c, seq_len, page_size)
+    if poison:
+        _poison_tail(c, seq_len, page_size)
     return IndexerInputs(q=q, c=c, seq_len=seq_len.astype(np.int32), page_size=page_size,
                          K=K, sorted=sorted_out, dtype=dtype, name=name)
 
@@ -250,8 +252,8 @@ class PrefillInputs:
 
 def make_prefill(B, T, H, D, N_pad, pos0, K, seed, dtype="bf16", sorted_out=False,
                  page_size=PAGE_SIZE, integer=False, name="custom"):
-    """q and c i.i.d. N(0,1) rounded to bf16 (or small integers); centroid rows
-    past the last token's block poisoned with a bf16 NaN."""
+    """q and c i.i.d. N(0,1), fp32 or rounded to bf16 (or small integers);
+    centroid rows past the last token's block poisoned with NaN."""
     rng = np.random.default_rng(seed)
     pos0 = np.asarray(pos0, dtype=np.int64)
     if integer:
@@ -263,7 +265,7 @@ def make_prefill(B, T, H, D, N_pad, pos0, K, seed, dtype="bf16", sorted_out=Fals
     if dtype == "bf16":
         q = f32_to_bf16_bits(q)
         c = f32_to_bf16_bits(c)
-        _poison_tail(c, np.maximum(pos0, 0) + T, page_size)
+    _poison_tail(c, np.maximum(pos0, 0) + T, page_size)
     return PrefillInputs(q=q, c=c, pos0=pos0.astype(np.int32), page_size=page_size, K=K,
                          sorted=sorted_out, dtype=dtype, name=name)
 
