@@ -28,6 +28,7 @@ constexpr int kTopkSplitMaxRows = 256;
 inline size_t topk_cand_offset() { return topk_ticket_bytes(kTopkSplitMaxRows); }
 constexpr int kTopkNT = 1024;   // top-K workgroup: 16 waves
 constexpr int kTopkSlots = 8;   // register tile: 1024*8*4 = 32768 keys
+constexpr int kSplitRep = 4;    // histogram copies of the split top-K merges' linear passes
 
 // ---- idx_topk ----------------------------------------------------------------------------
 // One workgroup of NT threads per row; rows longer than NT*SLOTS*4 keys are
@@ -84,6 +85,11 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     SelectSmem<kTopkNT, 2> s2;
   } smu;
   SelectSmem<kTopkNT, kTopkSlots>& sm = smu.s8;
+  // Index-order merges count their linear pass into kSplitRep histogram
+  // copies: quantised rows hand over candidates of two or three values, which
+  // put most lanes of a wave on the LDS words of two or three bins.
+  constexpr int HR = (SORTED || R8) ? 1 : kSplitRep;
+  __shared__ __attribute__((aligned(16))) uint32_t s_rep[HR > 1 ? HR * kRepStride : 4];
   __shared__ int s_last;
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
   const int b = blockIdx.x / S;
@@ -135,11 +141,11 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
   const MappedIdsOut out{ids + (size_t)b * K, ri};
   // the candidates of bf16 rows are bf16 values (in fp32): 16-bit keys
   if (MS == 2 || (MS == 0 && S * K <= kTopkNT * 2 * 4))
-    select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true, false, BF16IN, R8>(
-        rs, S * K, cstride, K, out, counts ? counts + b : nullptr, smu.s2, sort_lds);
+    select_row<kTopkNT, 2, SORTED, true, false, MappedIdsOut, true, false, BF16IN, R8, HR>(
+        rs, S * K, cstride, K, out, counts ? counts + b : nullptr, smu.s2, sort_lds, s_rep);
   else
-    select_row<kTopkNT, kTopkSlots, SORTED, true, false, MappedIdsOut, true, false, BF16IN, R8>(
-        rs, S * K, cstride, K, out, counts ? counts + b : nullptr, sm, sort_lds);
+    select_row<kTopkNT, kTopkSlots, SORTED, true, false, MappedIdsOut, true, false, BF16IN, R8,
+               HR>(rs, S * K, cstride, K, out, counts ? counts + b : nullptr, sm, sort_lds, s_rep);
 }
 
 // ---- idx_select: score chunks, the last-arriving workgroup of a request selects ---------

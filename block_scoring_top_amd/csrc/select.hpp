@@ -96,6 +96,13 @@ struct SelectSmem {
   uint32_t tot_gt, tot_eq;
 };
 
+// Copies of the linear pass's histogram (select_row's HREP > 1, for rows with
+// few distinct scores, whose lanes would otherwise queue on a few LDS words):
+// lane l adds to copy l % HREP, and copy r starts r * kRepStride words after
+// copy 0, so one bin of different copies sits in different LDS banks (kBins
+// is a multiple of the 32 banks; 8 more words move each copy by 8 banks).
+constexpr int kRepStride = kBins + 8;
+
 // Loads one register tile of keys. Every load of the tile is issued before any
 // is used (no branch between them), so the tile costs one memory round trip.
 // `cap` is the number of floats that may be read at `row` (>= n): when the row
@@ -677,8 +684,10 @@ __device__ __forceinline__ uint32_t refine_bin_bitonic(const uint32_t (&keys)[SL
 // results are read after the caller's next barrier. `clear` (may be null),
 // kBins words, is zeroed on the way. With `sfx` (kBins words, may be null),
 // sfx[b] gets the count of the bins above b and h is zeroed (for reuse as
-// per-bin counters).
-template <int NT, class SM>
+// per-bin counters). R > 1: h holds R copies of the histogram, copy r at
+// h + r * kRepStride, and a bin's count is the sum over the copies (only copy
+// 0 is zeroed for sfx).
+template <int NT, class SM, int R = 1>
 __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uint32_t* clear,
                                          uint32_t* sfx = nullptr) {
   constexpr int NW = NT / kWave;
@@ -688,14 +697,20 @@ __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uin
   const int lane = lane_id();
   const int top = kBins - (w * kWave + lane) * BPL;  // this lane's bins: [top - BPL, top)
   uint32_t c[BPL];  // c[k] = h[top - 1 - k]: descending
-  if constexpr (BPL == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(h + top - 2);
-    c[0] = v.y; c[1] = v.x;
-  } else {
 #pragma unroll
-    for (int r = 0; r < BPL / 4; ++r) {
-      const uint4 v = *reinterpret_cast<const uint4*>(h + top - 4 * (r + 1));
-      c[4 * r] = v.w; c[4 * r + 1] = v.z; c[4 * r + 2] = v.y; c[4 * r + 3] = v.x;
+  for (int k = 0; k < BPL; ++k) c[k] = 0u;
+#pragma unroll
+  for (int cp = 0; cp < R; ++cp) {
+    const uint32_t* hc = h + cp * kRepStride;
+    if constexpr (BPL == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(hc + top - 2);
+      c[0] += v.y; c[1] += v.x;
+    } else {
+#pragma unroll
+      for (int r = 0; r < BPL / 4; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(hc + top - 4 * (r + 1));
+        c[4 * r] += v.w; c[4 * r + 1] += v.z; c[4 * r + 2] += v.y; c[4 * r + 3] += v.x;
+      }
     }
   }
   uint32_t loc = 0;
@@ -745,13 +760,17 @@ __device__ __forceinline__ void find_bin(uint32_t* h, uint32_t need, SM& sm, uin
 // that of a bf16 score (bf16 rows, or candidates taken from them), so two
 // radix digits resolve a key. RADIX8: four 8-bit radix passes, no linear-bin
 // pass (the same results, for comparison).
+// HREP > 1: the linear pass counts into HREP copies of its histogram at hrep
+// (HREP * kRepStride words of LDS).
 template <int NT, int SLOTS, bool SORTED, bool COHERENT, bool BLOCKED, typename Out = IdsOut,
           bool ADAPTIVE = (!BLOCKED && SLOTS >= 8), bool BF16IN = false, bool KEY16 = BF16IN,
-          bool RADIX8 = false>
+          bool RADIX8 = false, int HREP = 1>
 __device__ __attribute__((always_inline)) void select_row(const void* row, int n, int cap, int K,
                                                          const Out& out, int32_t* count_out,
                                                          SelectSmem<NT, SLOTS>& sm,
-                                                         uint64_t* sortbuf) {
+                                                         uint64_t* sortbuf,
+                                                         uint32_t* hrep = nullptr) {
+  static_assert(HREP == 1 || HREP == 2 || HREP == 4 || HREP == 8, "1, 2, 4 or 8 copies");
   constexpr int NW = NT / kWave;
   constexpr int TILE = NT * SLOTS * 4;
   constexpr int E = SLOTS * NW;
@@ -839,6 +858,12 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
     }
   }
   for (int i = t; i < 2 * kBins; i += NT) (&sm.hist[0][0])[i] = 0u;
+  if constexpr (HREP > 1) {
+    static_assert(kRepStride % 4 == 0, "the copies are cleared as 16-byte words");
+    if (upfront)
+      for (int i = t; i < HREP * kRepStride / 4; i += NT)
+        reinterpret_cast<uint4*>(hrep)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   __syncthreads();
 
   uint32_t prefix = 0, need = (uint32_t)K, ncand = 0;
@@ -895,6 +920,8 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
                       lo, by_key};
       bin_map = bm;
       uint32_t* h = sm.hist[0];
+      // this lane's copy of the histogram
+      uint32_t* hl = HREP > 1 ? hrep + (lane & (HREP - 1)) * kRepStride : h;
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
         if (!slot_live(0, i)) continue;
@@ -915,7 +942,7 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
           // Rows whose scores all share one bin except an outlier's, and
           // quantised rows, measured the same as with merged adds of shared
           // bins.
-          if (act) atomicAdd(&h[bin], 1u);
+          if (act) atomicAdd(&hl[bin], 1u);
         }
       }
       if (t == 0) {
@@ -924,10 +951,13 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
         sm.bin_max = 0u;
       }
       __syncthreads();
+      // with copies, histogram 0 stays zero (as find_bin leaves it for the
+      // score-ordered counters, and as the radix passes expect it)
       if constexpr (SORTED)
-        find_bin<NT>(h, need, sm, nullptr, sm.hist[1]);
+        find_bin<NT, SelectSmem<NT, SLOTS>, HREP>(HREP > 1 ? hrep : h, need, sm, nullptr,
+                                                  sm.hist[1]);
       else
-        find_bin<NT>(h, need, sm, sm.hist[1]);
+        find_bin<NT, SelectSmem<NT, SLOTS>, HREP>(HREP > 1 ? hrep : h, need, sm, sm.hist[1]);
       __syncthreads();
       ncand = sm.n_cand;
       const uint32_t sb = sm.sel_bin, bneed = sm.sel_need, btot = sm.sel_tot;
