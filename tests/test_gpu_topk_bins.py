@@ -62,3 +62,36 @@ def test_topk_heavy_tailed_and_tied_rows(N, K, sorted_out):
     ids, counts = idx.idx_topk(to_dev(s), K, to_dev(nv.astype(np.int32)), sorted_out)
     torch.cuda.synchronize()
     check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, sorted_out)
+
+
+def few_valued_rows(rng, B, n):
+    """Rows of 2, 3, 5 or 8 distinct small-integer values (exact in bf16): the
+    split top-K's segments then hand over candidates of two or three values,
+    whose linear-bin counts the merge spreads over several histogram copies.
+    Values 0, 1, 2 put the candidates in bins 0, 1024 and 2047 (one LDS bank
+    in a single copy)."""
+    rows = []
+    for r in range(B):
+        nvals = (2, 3, 5, 8)[r % 4]
+        row = rng.integers(0, nvals, n).astype(np.float32)
+        if r % 8 >= 4:
+            row -= np.float32(nvals // 2)   # values of both signs
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 300, 2048])
+def test_topk_split_few_valued_rows(dtype, K):
+    N, B = 30000, 16
+    rng = np.random.default_rng(910 + K)
+    s = few_valued_rows(rng, B, N)
+    nv = np.full(B, N, dtype=np.int64)
+    nv[3::5] = rng.integers(K + 1, N, len(nv[3::5]))
+    say(f"[topk few values] {dtype} N={N} K={K} rows={B}")
+    t = to_dev(s)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)  # small integers: exact
+    ids, counts = idx.idx_topk(t, K, to_dev(nv.astype(np.int32)))
+    torch.cuda.synchronize()
+    check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, False)
