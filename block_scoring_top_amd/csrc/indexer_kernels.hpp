@@ -85,10 +85,11 @@ __global__ __launch_bounds__(kTopkNT) void topk_split_kernel(
     SelectSmem<kTopkNT, 2> s2;
   } smu;
   SelectSmem<kTopkNT, kTopkSlots>& sm = smu.s8;
-  // Index-order merges count their linear pass into kSplitRep histogram
-  // copies: quantised rows hand over candidates of two or three values, which
-  // put most lanes of a wave on the LDS words of two or three bins.
-  constexpr int HR = (SORTED || R8) ? 1 : kSplitRep;
+  // The merges count their linear pass into kSplitRep histogram copies:
+  // quantised rows hand over candidates of two or three values, which put most
+  // lanes of a wave on the LDS words of two or three bins. (With the sort
+  // buffer of a score-ordered merge the workgroup takes 67-83 KB of LDS.)
+  constexpr int HR = R8 ? 1 : kSplitRep;
   __shared__ __attribute__((aligned(16))) uint32_t s_rep[HR > 1 ? HR * kRepStride : 4];
   __shared__ int s_last;
   extern __shared__ uint64_t sort_lds[];  // sort_lds_bytes(K) when SORTED
