@@ -1350,6 +1350,11 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
     carry_eq += sm.tot_eq;
   }
 
+  // Every taken key is the one threshold key (no key above a one-key band):
+  // the pairs were placed in index order, which for equal keys is the score
+  // order (ties to the lower id), so they need no sort.
+  const bool one_key = !BLOCKED && !by_bins && !simple && lo_b == hi_b && carry_gt == 0u;
+
   for (int k = (int)m_out + t; k < K; k += NT) out.pad(k);
   if (count_out != nullptr && t == 0) *count_out = (int32_t)m_out;
 
@@ -1366,6 +1371,12 @@ __device__ __attribute__((always_inline)) void select_row(const void* row, int n
         rank_in_bins<NT, 2>(sortbuf, (int)m_out, bin_map, sm.hist[0], sm.hist[1], out);
       } else {
         rank_in_bins<NT, 4>(sortbuf, (int)m_out, bin_map, sm.hist[0], sm.hist[1], out);
+      }
+    } else if (one_key) {
+      __syncthreads();  // every pair is in sortbuf
+      for (int i = t; i < (int)m_out; i += NT) {
+        const uint64_t v = sortbuf[i];
+        out.put(i, (int32_t)~(uint32_t)v, (uint32_t)(v >> 32));
       }
     } else {
       // zero (below every key) pads the sort up to a power of two
