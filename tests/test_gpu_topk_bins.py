@@ -95,3 +95,26 @@ def test_topk_split_few_valued_rows(dtype, K):
     ids, counts = idx.idx_topk(t, K, to_dev(nv.astype(np.int32)))
     torch.cuda.synchronize()
     check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, False)
+
+
+@pytest.mark.parametrize("N,B", [(30000, 16), (8000, 8)])
+@pytest.mark.parametrize("K", [300, 2048])
+def test_topk_score_order_top_value_copies(N, B, K):
+    """Score order where the row's top value has K - 1, K, K + 1 or 3K copies
+    (and rows of one value): when the copies fill K, every taken key is that
+    value and the pairs stand in index order without a sort; with K - 1 copies
+    one lower key joins them and the sort runs."""
+    rng = np.random.default_rng(977 + N + K)
+    rows = []
+    for r in range(B):
+        c = (K - 1, K, K + 1, 3 * K, N)[r % 5]
+        row = (rng.standard_normal(N) - 10.0).astype(np.float32)
+        row[rng.choice(N, c, replace=False)] = 5.0
+        rows.append(row)
+    s = np.stack(rows)
+    nv = np.full(B, N, dtype=np.int64)
+    nv[2::3] = rng.integers(K + 1, N, len(nv[2::3]))
+    say(f"[topk top-value copies] N={N} K={K} rows={B}")
+    ids, counts = idx.idx_topk(to_dev(s), K, to_dev(nv.astype(np.int32)), True)
+    torch.cuda.synchronize()
+    check_ids_exact(ids.cpu().numpy(), counts.cpu().numpy(), s, nv, K, True)
